@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 MLA decode step on one MI355X.
+
+Step (timed unit): one decode serving step of the dense workload B=64
+sequences x 128 heads x 4096 cached tokens (pages of 64, 432-byte records,
+4 splits + merge): the NVFP4 cache write of the batch's 64 new tokens
+followed by the paged split-K decode (one kernel, merge fused).  Inputs are
+resident in HBM before timing starts; the cache is rotated over 4 copies
+(> 256 MB Infinity Cache) so that decode reads come from HBM.
+
+Printed: one JSON line with queries/s (B / step time), the roofline of the
+decode kernel (HIP events around every timed launch, on the launch stream),
+the oracle's CPU throughput on a bounded sample, and extra lines for the
+other paths (16-head decode, top-k sparse decode, prefill).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mla_attention_nvfp4_amd import ops, workloads  # noqa: E402
+
+METRIC = "NVFP4 MLA decode HBM GB/s & % roofline; queries/s at B=64, L=4k, 128 heads"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+ROTATE = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(inp, n_tokens_total: int, H: int) -> int:
+    """Algorithmic bytes of one decode launch: records read, q read, out and
+    lse written, page-table entries and seq_lens read."""
+    B = inp.B
+    pages = sum(math.ceil(int(L) / inp.page_size) for L in inp.seq_lens)
+    return (n_tokens_total * inp.record_bytes + B * H * 576 * 2 + B * H * 512 * 4 + B * H * 4
+            + pages * 4 + B * 4)
+
+
+def decode_flops(n_tokens_total: int, H: int) -> float:
+    return 2.0 * H * n_tokens_total * (576 + 512)
+
+
+class DecodeBench:
+    """Device-resident decode workload with a rotated cache."""
+
+    def __init__(self, inp, rotate: int, sparse: bool = False):
+        self.inp = inp
+        dev = "cuda"
+        base = torch.zeros((inp.num_pages, inp.page_size, inp.record_bytes), dtype=torch.uint8, device=dev)
+        ops.cache_write(inp.kv_c.to(dev), inp.k_pe.to(dev), inp.slot_mapping.to(dev), base, inp.outer_scale)
+        self.caches = [base] + [base.clone() for _ in range(0 if sparse else rotate - 1)]
+        self.n_rot = rotate
+        q = inp.q.to(dev)
+        self.q_nope, self.q_rope = q[..., :512], q[..., 512:]
+        self.pt = inp.page_table.to(dev)
+        self.seq = inp.seq_lens.to(dev)
+        # sparse: rotate index sets instead of caches (valid entries shifted
+        # by a per-set offset modulo L, so each set gathers other records)
+        self.idx = None
+        if sparse:
+            L = inp.seq_lens.to(torch.int64)[:, None]
+            base_idx = inp.indices.to(torch.int64)
+            sets = []
+            for k in range(rotate):
+                shifted = torch.where(base_idx >= 0, (base_idx + k * 5461) % L, base_idx)
+                sets.append(shifted.to(torch.int32).to(dev))
+            self.idx = sets
+        B, H = inp.B, inp.H
+        self.out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        need = ops.decode_workspace_bytes(B, H, inp.max_splits)
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+        # the step's new tokens overwrite the last position of every sequence
+        g = torch.Generator().manual_seed(1234)
+        self.new_kv = torch.randn((B, 576), generator=g).to(torch.bfloat16).to(dev)
+        last = inp.token_offsets[1:] - 1
+        self.new_slots = inp.slot_mapping[last].to(dev)
+        torch.cuda.synchronize()
+
+    def write(self, r):
+        ops.cache_write(self.new_kv[:, :512], self.new_kv[:, 512:], self.new_slots, self.caches[r],
+                        self.inp.outer_scale)
+
+    def decode(self, r):
+        inp = self.inp
+        if self.idx is None:
+            ops.decode(self.q_nope, self.q_rope, self.caches[r], self.pt, self.seq, inp.outer_scale,
+                       inp.softmax_scale, inp.max_splits, out=self.out, lse=self.lse, workspace=self.ws)
+        else:
+            ops.sparse_decode(self.q_nope, self.q_rope, self.caches[0], self.pt, self.seq, self.idx[r],
+                              inp.outer_scale, inp.softmax_scale, inp.max_splits, out=self.out, lse=self.lse,
+                              workspace=self.ws)
+
+    def run(self, steps: int, warmup: int, with_write: bool = True):
+        """Returns (ms per step from the host clock, mean decode-kernel ms from HIP events)."""
+        stream = torch.cuda.current_stream()
+        for i in range(warmup):
+            if with_write:
+                self.write(i % self.n_rot)
+            self.decode(i % self.n_rot)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            r = i % self.n_rot
+            if with_write:
+                self.write(r)
+            ev[i][0].record(stream)
+            self.decode(r)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        k_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        return (t1 - t0) * 1e3 / steps, k_ms
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """The oracle (unchanged) on whole sequences of the same workload, until
+    the time budget is used: queries/s on the host cores."""
+    from oracle import decode as OD
+    from oracle import record as OR
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = inp.q.float().numpy()
+    offs = inp.token_offsets.numpy()
+    done = 0
+    t0 = time.perf_counter()
+    while done < inp.B and (done == 0 or time.perf_counter() - t0 < budget_s):
+        b = done
+        cache = np.zeros((inp.num_pages, inp.page_size, inp.record_bytes), np.uint8)
+        rows = np.arange(offs[b], offs[b + 1])
+        kv = inp.kv_c[rows].contiguous().view(torch.int16).numpy().view(np.uint16)
+        pe = inp.k_pe[rows].contiguous().view(torch.int16).numpy().view(np.uint16)
+        OR.cache_write(cache, kv, pe, inp.slot_mapping.numpy()[rows], inp.outer_scale)
+        OD.dense_decode(q[..., :512], q[..., 512:], cache, inp.page_table.numpy(), inp.seq_lens.numpy(),
+                        inp.page_size, inp.outer_scale, inp.softmax_scale, batch=[b])
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {inp.B} sequences (all {inp.H} heads, L={int(inp.seq_lens[0])}): oracle "
+                      f"cache write of their tokens + fp64 decode, {el:.1f} s; host cpu_count={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 16-head, sparse and prefill lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is measured "
+              f"on one GPU's share, see the sharding notes in DESIGN.md", flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", flush=True)
+        sys.exit(2)
+
+    log("generating decode workload 1 (B=64, H=128, L=4096)")
+    inp = workloads.decode_workload(1)
+    H, B = inp.H, inp.B
+    ntok = int(inp.seq_lens.sum())
+    bench = DecodeBench(inp, ROTATE)
+    ms_step, k_ms = bench.run(args.steps, args.warmup)
+    flops = decode_flops(ntok, H)
+    nbytes = decode_bytes(inp, ntok, H)
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    gbps = nbytes / (k_ms * 1e-3) / 1e9
+    log(f"decode kernel {k_ms * 1e3:.1f} us, step {ms_step * 1e3:.1f} us, {tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense NVFP4 MLA decode step: B=64, H=128, L=4096, page 64, 432-byte records, "
+                               "4 splits + fused merge, plus NVFP4 cache write of 64 new tokens",
+                   "global_batch": B, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "decode_kernel", "kernel_us": k_ms * 1e3,
+                     "flops_per_launch": flops, "bytes_per_launch": nbytes},
+        "hbm": {"achieved_gbps": gbps, "peak_gbps": PEAK_HBM_GBPS, "frac": gbps / PEAK_HBM_GBPS},
+    }
+    del bench
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        paths = {}
+        log("16-head decode (workload 1 shape, H=16)")
+        inp16 = workloads.decode_workload(1, H=16)
+        b16 = DecodeBench(inp16, ROTATE)
+        _, k16 = b16.run(max(10, args.steps // 2), 5, with_write=False)
+        by = decode_bytes(inp16, ntok, 16)
+        paths["decode_H16"] = {"kernel_us": k16 * 1e3, "gbps": by / (k16 * 1e-3) / 1e9,
+                               "frac_hbm": by / (k16 * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                               "queries_per_s": inp16.B / (k16 * 1e-3)}
+        del b16, inp16
+        torch.cuda.empty_cache()
+        log("sparse top-k decode (workload 3)")
+        inp3 = workloads.decode_workload(3)
+        b3 = DecodeBench(inp3, 12, sparse=True)
+        _, k3 = b3.run(max(10, args.steps // 2), 5, with_write=False)
+        idx = inp3.indices
+        nvalid = int(((idx >= 0) & (idx < inp3.seq_lens[:, None])).sum())
+        f3 = decode_flops(nvalid, inp3.H)
+        paths["sparse_decode"] = {"kernel_us": k3 * 1e3, "tflops": f3 / (k3 * 1e-3) / 1e12,
+                                  "frac_mfma": f3 / (k3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                  "queries_per_s": inp3.B / (k3 * 1e-3), "valid_indices": nvalid}
+        del b3, inp3
+        torch.cuda.empty_cache()
+        result["paths"] = paths
+
+    if not args.no_cpu:
+        log("oracle CPU baseline")
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * mla_nvfp4.h -- C ABI of the NVFP4 MLA attention library for AMD Instinct
+ * MI355X (gfx950): libmla_nvfp4.so.
+ *
+ * DeepSeek-style multi-head latent attention (MLA) whose latent KV cache is
+ * stored as NVFP4: 512 e2m1 codes two per byte, one e4m3 scale per 16
+ * elements, a per-layer fp32 outer scale, and a 64-d RoPE part in bf16 or
+ * e4m3.  The pages this interface follows, cited by title and section:
+ *
+ *  [FUSED-OUT] vLLM pull request "feat: MLA prefill NVFP4 fused output"
+ *  [MO-MLA]    Model-Optimizer pull request "Add NVFP4/FP8 Q/K/P/V + 2:4
+ *              attention quantization for MLA (vLLM TRITON_MLA)"
+ *  [B12X]      b12x pull request "nvfp4 MLA KV cache + per-layer outer-scale +
+ *              fp8-RoPE KV-cell (sm120)"
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; it enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL is the null stream) and returns at once.
+ *    Results are ordered on that stream.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Strides are in
+ *    elements.  All other tensors are dense row-major as stated.
+ *  - Return value: MLA_OK (0) or a negative mla_status.  Arguments are
+ *    validated on the host before anything is enqueued; on error nothing is
+ *    enqueued and mla_last_error() (thread-local) describes the problem.
+ *  - Device-side preconditions that are not checked on the host are listed
+ *    per call; where a cheap check avoids an out-of-bounds access the kernel
+ *    performs it and skips the offending element instead.
+ *  - Only gfx950 devices are supported (MLA_ERR_UNSUPPORTED_DEVICE otherwise),
+ *    the analogue of [B12X], review 1's point that the NVFP4 kernels need a
+ *    guard for the one architecture they were built for.
+ */
+#ifndef MLA_NVFP4_H
+#define MLA_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARGUMENT = -1,
+    MLA_ERR_RECORD_BYTES = -2,       /* record width not 368 or 432 */
+    MLA_ERR_UNSUPPORTED_DEVICE = -3, /* current device is not gfx950 */
+    MLA_ERR_WORKSPACE_TOO_SMALL = -4,
+    MLA_ERR_HIP = -5,                /* a HIP runtime call failed */
+    MLA_ERR_UNSUPPORTED = -6         /* valid request this build cannot serve */
+} mla_status;
+
+/* Fixed geometry of the latent ([MO-MLA], PR body: absorbed decode over a
+ * 512-d latent plus 64-d RoPE; [B12X], review 1: records of 432/368 bytes). */
+#define MLA_D_LATENT 512
+#define MLA_D_ROPE 64
+#define MLA_RECORD_BYTES_BF16_ROPE 432
+#define MLA_RECORD_BYTES_FP8_ROPE 368
+/* Prefill head dims ([MO-MLA], commit 1: asymmetric 192/128 head dims). */
+#define MLA_PREFILL_D_QK 192
+#define MLA_PREFILL_D_V 128
+/* Key-tile width of the prefill P-quantization schedule (see
+ * mla_prefill_nvfp4_out). */
+#define MLA_PREFILL_P_TILE 64
+/* Decode splits cover at least this many tokens (see mla_decode_num_splits). */
+#define MLA_DECODE_MIN_SPLIT_TOKENS 256
+
+/* qdq_flags bits of mla_prefill_nvfp4_out. */
+#define MLA_QDQ_Q 1u
+#define MLA_QDQ_K 2u
+#define MLA_QDQ_P 4u
+#define MLA_QDQ_V 8u
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Record width for a RoPE part in e4m3 (rope_fp8 != 0: 368) or bf16 (432).
+ * [B12X], review 1: the record width is the authoritative ABI and decides
+ * the RoPE storage type. */
+int mla_nvfp4_record_bytes(int rope_fp8);
+
+/* Number of split-K chunks decode uses for a sequence of `seq_len` tokens
+ * (or a top-k list of `seq_len` entries) with at most `max_splits` chunks:
+ * want = clamp(ceil(seq_len / MLA_DECODE_MIN_SPLIT_TOKENS), 1, max_splits),
+ * chunk = ceil(ceil(seq_len/64) / want) tiles of 64 tokens, result =
+ * ceil(ceil(seq_len/64) / chunk) (never an empty chunk); 1 for seq_len <= 0.
+ * The kernels evaluate the same function on the device. */
+int mla_decode_num_splits(int seq_len, int max_splits);
+
+/* Bytes of decode workspace for B sequences, H heads, max_splits chunks:
+ * partial outputs fp32 [B][max_splits][H][512], partial LSE fp32
+ * [B][max_splits][H], then int32 arrival counters [B][ceil(H/16)], each
+ * region 256-byte aligned.  0 when max_splits <= 1.  The workspace must be
+ * zero-filled before its first use; every completed call leaves the counters
+ * at zero again, so one workspace serves any number of stream-ordered calls
+ * (calls that may run concurrently need separate workspaces). */
+size_t mla_decode_workspace_bytes(int B, int H, int max_splits);
+
+/* Bytes of a 128x4-swizzled e4m3 scale buffer for `rows` rows of
+ * `scale_cols` scales: ceil(rows/128)*128 * (ceil(scale_cols/4)*4). */
+size_t mla_nvfp4_swizzled_scale_bytes(int64_t rows, int64_t scale_cols);
+
+/* Write T tokens into the NVFP4 latent cache.
+ * [MO-MLA], commits 1-2 (the latent is quantized once, before the cache
+ * write, and decode consumes that representation as is); [B12X], PR
+ * description (NVFP4 latent with a per-layer fp32 outer scale; optional fp8
+ * RoPE cell).
+ *
+ *  kv_c          bf16 [T, 512], row stride kv_c_row_stride (multiple of 8),
+ *                16-byte aligned
+ *  k_pe          bf16 [T, 64], row stride k_pe_row_stride (even), 4-byte
+ *                aligned
+ *  slot_mapping  int64 [T]: destination slot of token t; a slot < 0 or
+ *                >= num_slots skips the token
+ *  cache         uint8 [num_slots, record_bytes], 16-byte aligned
+ *  record_bytes  432 (bf16 RoPE) or 368 (e4m3 RoPE), else MLA_ERR_RECORD_BYTES
+ *  outer_scale   the latent's dequant multiplier g (finite, > 0)
+ *
+ * Record layout: bytes [0,256) codes, element 2i in the low nibble of byte i;
+ * [256,288) 32 e4m3 block scales; then 64 RoPE values (bf16 little-endian, or
+ * e4m3 RNE-satfinite of the bf16 value, unscaled); last 16 bytes zero.  Per
+ * block of 16: a = max|x|, t = a / (6 g), s = e4m3(t) (RNE, satfinite),
+ * d = s * g, code_i = e2m1(x_i * (d == 0 ? 0 : 1/d)) (RNE, satfinite, sign
+ * kept), each step one IEEE fp32 operation.  T == 0 is a no-op.
+ * Precondition (unchecked): no two tokens share a slot. */
+int mla_nvfp4_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride,
+                          const uint16_t* k_pe, int64_t k_pe_row_stride,
+                          const int64_t* slot_mapping, int64_t T,
+                          uint8_t* cache, int64_t num_slots, int record_bytes,
+                          float outer_scale, void* stream);
+
+/* Dense absorbed split-K decode over the paged NVFP4 latent cache.
+ * [MO-MLA], commit 1 (split-K absorbed decode over the paged latent with
+ * grouped query heads; natural-log LSE for merging) and commit 3 (V is the
+ * stored latent itself); [B12X], walkthrough (stage, dequantize, accumulate;
+ * outer scale restored on read) and review 2 (Q is bf16, unquantized).
+ *
+ * For sequence b (L = min(seq_lens[b], max_pages_per_seq * page_size)) and
+ * head h, token j < L is record page_table[b][j / page_size] * page_size +
+ * j % page_size of the cache.  With k_j = outer_scale * dequant(latent_j),
+ * r_j the RoPE part:  z_j = softmax_scale * (q_nope . k_j + q_rope . r_j),
+ * out[b][h] = sum_j e^(z_j - m) k_j / sum_j e^(z_j - m), lse[b][h] = m +
+ * ln sum_j e^(z_j - m).  L == 0 gives out = 0, lse = -inf.
+ *
+ *  q_nope, q_rope  bf16 [B, H, 512] and [B, H, 64] with common strides
+ *                  q_stride_b, q_stride_h (multiples of 8; 16-byte aligned)
+ *  cache           uint8 [num_pages * page_size, record_bytes]
+ *  page_table      int32 [B, max_pages_per_seq]
+ *  seq_lens        int32 [B]
+ *  max_splits      >= 1; sequence b is split into
+ *                  mla_decode_num_splits(L, max_splits) chunks whose
+ *                  (out, lse) partials are merged as mla_lse_merge does
+ *  workspace       >= mla_decode_workspace_bytes(B, H, max_splits) bytes,
+ *                  zero-filled before first use (may be NULL when
+ *                  max_splits == 1)
+ *  out, lse        fp32 [B, H, 512] and [B, H]
+ *
+ * Kernel-side checks: a page id outside [0, num_pages) masks that token.
+ * One launch on `stream`; within it the last workgroup to finish a
+ * sequence's chunks merges them in chunk order (bitwise deterministic). */
+int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
+                     int64_t q_stride_b, int64_t q_stride_h,
+                     const uint8_t* cache, int64_t num_pages, int record_bytes,
+                     int page_size, const int32_t* page_table, int max_pages_per_seq,
+                     const int32_t* seq_lens, int B, int H,
+                     float outer_scale, float softmax_scale, int max_splits,
+                     void* workspace, size_t workspace_bytes,
+                     float* out, float* lse, void* stream);
+
+/* Top-k sparse decode: as mla_decode_nvfp4, but sequence b attends only to
+ * the tokens listed in indices[b][0..topk).  [B12X], walkthrough and
+ * sequence diagram (sparse MLA decode on the NVFP4 cache with the latent
+ * scale).  Entries are logical token positions of sequence b, shared by all
+ * heads; an entry < 0 or >= L is masked; a position listed twice counts
+ * twice; no valid entry gives out = 0, lse = -inf.  Splits run over the
+ * index list: mla_decode_num_splits(topk, max_splits) chunks.
+ *
+ *  indices    int32 [B, topk] (dense rows), topk >= 1
+ *  workspace  >= mla_decode_workspace_bytes(B, H, max_splits) bytes, as for
+ *             mla_decode_nvfp4 */
+int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
+                            int64_t q_stride_b, int64_t q_stride_h,
+                            const uint8_t* cache, int64_t num_pages, int record_bytes,
+                            int page_size, const int32_t* page_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int H,
+                            float outer_scale, float softmax_scale,
+                            const int32_t* indices, int topk, int max_splits,
+                            void* workspace, size_t workspace_bytes,
+                            float* out, float* lse, void* stream);
+
+/* Merge S partial attention results over disjoint token sets.  [MO-MLA],
+ * commit 1: natural-log LSE "for chunked-context merging".  For each (b, h)
+ * with n = splits_per_seq[b] (clamped to [0, S]; all S when the pointer is
+ * NULL): M = max_{s<n} lse_s; if n == 0 or M == -inf, out = 0 and lse = -inf;
+ * else w_s = e^(lse_s - M), out = sum w_s out_s / sum w_s, lse = M + ln sum w_s.
+ *
+ *  partial_out  fp32 [B, S, H, D];  partial_lse fp32 [B, S, H]
+ *  out          fp32 [B, H, D];     lse fp32 [B, H] or NULL
+ *  D            multiple of 4, 1..4096 */
+int mla_lse_merge(const float* partial_out, const float* partial_lse,
+                  const int32_t* splits_per_seq, int B, int S, int H, int D,
+                  float* out, float* lse, void* stream);
+
+/* Varlen causal MLA prefill with NVFP4 fake quantization of Q/K/P/V and the
+ * output written directly as NVFP4.  [MO-MLA], commit 1 and PR body (varlen
+ * prefill, qk 192 / v 128, every matmul operand quantized once along its own
+ * contraction axis in 1x16 NVFP4 blocks, P quantized after the softmax row
+ * sum with the denominator unquantized, natural-log LSE); [FUSED-OUT], PR
+ * description (packed e2m1 output, 128x4-swizzled e4m3 scales, fp32 global
+ * scale, the separate quantization pass removed).
+ *
+ * Sequence n covers rows [cu_seqlens[n], cu_seqlens[n+1]); queries and keys
+ * of a sequence coincide; row i attends to keys j <= i.  Flags (MLA_QDQ_*):
+ * Q and K quantized along the head dim (12 blocks of 16) with multipliers
+ * g_q, g_k; V along local token position (blocks [16k,16k+16) from the
+ * sequence start, the last one possibly short) per head and dim, with g_v;
+ * P along keys with g_p, in blocks aligned to the local key index.  Keys are
+ * visited in tiles of MLA_PREFILL_P_TILE = 64 from key 0; the running max is
+ * refreshed per tile and P is quantized against it (the schedule is part of
+ * the definition when MLA_QDQ_P is set).  O = acc / l, LSE = m + ln l, and
+ * each 128-d output row (t, h) is quantized in 8 blocks of 16 with
+ * multiplier out_global_scale: codes to out_fp4[t][h][0..64) (element 2i low
+ * nibble), scales at the swizzled offset of SF[t][8h + blk] with SF having
+ * H*8 columns; padding rows of the last 128-row tile are written as zero.
+ *
+ *  q, k         bf16 [T, H, 192], strides (q_stride_t, q_stride_h) and
+ *               (k_stride_t, k_stride_h), multiples of 8, 16-byte aligned
+ *  v            bf16 [T, H, 128], strides (v_stride_t, v_stride_h), same rule
+ *  cu_seqlens   int32 [N + 1], non-decreasing, cu[0] = 0, cu[N] = T
+ *  max_seqlen   >= every sequence length
+ *  g_*          finite, > 0 (ignored when the flag is off)
+ *  workspace    >= mla_prefill_workspace_bytes(T, H, qdq_flags) bytes
+ *  out_fp4      uint8 [T, H, 64]
+ *  out_scales   uint8, mla_nvfp4_swizzled_scale_bytes(T, H * 8) bytes
+ *  lse          fp32 [T, H] or NULL
+ * Precondition (unchecked): cu_seqlens as stated. */
+size_t mla_prefill_workspace_bytes(int64_t T, int H, unsigned qdq_flags);
+int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h,
+                          const uint16_t* k, int64_t k_stride_t, int64_t k_stride_h,
+                          const uint16_t* v, int64_t v_stride_t, int64_t v_stride_h,
+                          const int32_t* cu_seqlens, int N, int max_seqlen,
+                          int64_t T, int H, float softmax_scale, unsigned qdq_flags,
+                          float g_q, float g_k, float g_v, float g_p,
+                          float out_global_scale,
+                          void* workspace, size_t workspace_bytes,
+                          uint8_t* out_fp4, uint8_t* out_scales, float* lse,
+                          void* stream);
+
+/* NVFP4 quantization of fp32 rows with swizzled scales: the stand-alone
+ * quantization pass that [FUSED-OUT] (PR description) folds into the prefill
+ * epilogue, exposed so the epilogue's arithmetic and layout can be checked
+ * bit for bit.  Same per-block rule as the prefill output with multiplier
+ * global_scale.
+ *
+ *  x               fp32 [M, K] dense, K a multiple of 16, 1..65536
+ *  codes           uint8 [M, K/2]
+ *  scales_swizzled uint8, mla_nvfp4_swizzled_scale_bytes(M, K/16) bytes;
+ *                  padding rows and columns are written as zero */
+int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale,
+                            uint8_t* codes, uint8_t* scales_swizzled, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_NVFP4_H */

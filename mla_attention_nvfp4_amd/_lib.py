@@ -1,0 +1,250 @@
+"""ctypes binding of libmla_nvfp4.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module checks
+tensor dtypes, devices and shapes, passes raw device pointers and the current
+HIP stream, and turns a negative status into ``MlaError``.  There is no CPU
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_nvfp4.so")
+
+c_int, c_i64, c_u32, c_f32, c_sz, c_p = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_float,
+                                         ctypes.c_size_t, ctypes.c_void_p)
+
+# name -> (restype, argtypes); mirrors include/mla_nvfp4.h
+SIGNATURES = {
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_nvfp4_record_bytes": (c_int, [c_int]),
+    "mla_decode_num_splits": (c_int, [c_int, c_int]),
+    "mla_decode_workspace_bytes": (c_sz, [c_int, c_int, c_int]),
+    "mla_nvfp4_swizzled_scale_bytes": (c_sz, [c_i64, c_i64]),
+    "mla_nvfp4_cache_write": (c_int, [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_int, c_f32, c_p]),
+    "mla_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_int,
+                                 c_int, c_f32, c_f32, c_int, c_p, c_sz, c_p, c_p, c_p]),
+    "mla_sparse_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p,
+                                        c_int, c_int, c_f32, c_f32, c_p, c_int, c_int, c_p, c_sz, c_p, c_p,
+                                        c_p]),
+    "mla_lse_merge": (c_int, [c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_p, c_p, c_p]),
+    "mla_prefill_workspace_bytes": (c_sz, [c_i64, c_int, c_u32]),
+    "mla_prefill_nvfp4_out": (c_int, [c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_int,
+                                      c_int, c_i64, c_int, c_f32, c_u32, c_f32, c_f32, c_f32, c_f32, c_f32,
+                                      c_p, c_sz, c_p, c_p, c_p, c_p]),
+    "mla_nvfp4_quantize_rows": (c_int, [c_p, c_i64, c_int, c_f32, c_p, c_p, c_p]),
+}
+
+MLA_QDQ_Q, MLA_QDQ_K, MLA_QDQ_P, MLA_QDQ_V = 1, 2, 4, 8
+PREFILL_P_TILE = 64
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mla status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m mla_attention_nvfp4_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MlaError(rc, lib().mla_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} tensor on a GPU")
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+# ---------------------------------------------------------------- helpers --
+
+def record_bytes(rope_fp8: bool) -> int:
+    return lib().mla_nvfp4_record_bytes(1 if rope_fp8 else 0)
+
+
+def decode_num_splits(n: int, max_splits: int) -> int:
+    return lib().mla_decode_num_splits(int(n), int(max_splits))
+
+
+def decode_workspace_bytes(B: int, H: int, max_splits: int) -> int:
+    return lib().mla_decode_workspace_bytes(B, H, max_splits)
+
+
+def swizzled_scale_bytes(rows: int, scale_cols: int) -> int:
+    return lib().mla_nvfp4_swizzled_scale_bytes(rows, scale_cols)
+
+
+def prefill_workspace_bytes(T: int, H: int, flags: int) -> int:
+    return lib().mla_prefill_workspace_bytes(T, H, flags)
+
+
+# ------------------------------------------------------------------ calls --
+
+def cache_write(kv_c, k_pe, slot_mapping, cache, outer_scale: float) -> None:
+    """kv_c bf16 [T,512], k_pe bf16 [T,64] (row-strided), slot_mapping int64 [T],
+    cache uint8 [..., record_bytes] contiguous."""
+    _need(kv_c, torch.bfloat16, "kv_c")
+    _need(k_pe, torch.bfloat16, "k_pe")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(cache, torch.uint8, "cache")
+    if kv_c.dim() != 2 or kv_c.shape[1] != 512 or kv_c.stride(1) != 1:
+        raise ValueError("kv_c must be [T, 512] with unit inner stride")
+    if k_pe.dim() != 2 or k_pe.shape[1] != 64 or k_pe.stride(1) != 1 or k_pe.shape[0] != kv_c.shape[0]:
+        raise ValueError("k_pe must be [T, 64] with unit inner stride")
+    if not cache.is_contiguous() or slot_mapping.numel() != kv_c.shape[0]:
+        raise ValueError("cache must be contiguous and slot_mapping [T]")
+    rec = cache.shape[-1]
+    _check(lib().mla_nvfp4_cache_write(kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0),
+                                       slot_mapping.data_ptr(), kv_c.shape[0], cache.data_ptr(),
+                                       cache.numel() // rec, rec, float(outer_scale), _stream(cache)))
+
+
+def _decode_common(q_nope, q_rope, cache, page_table, seq_lens):
+    for t, n, d in ((q_nope, "q_nope", torch.bfloat16), (q_rope, "q_rope", torch.bfloat16),
+                    (cache, "cache", torch.uint8), (page_table, "page_table", torch.int32),
+                    (seq_lens, "seq_lens", torch.int32)):
+        _need(t, d, n)
+    if q_nope.dim() != 3 or q_nope.shape[2] != 512 or q_rope.shape[:2] != q_nope.shape[:2] \
+            or q_rope.shape[2] != 64 or q_nope.stride() != q_rope.stride() or q_nope.stride(2) != 1:
+        raise ValueError("q_nope [B,H,512] and q_rope [B,H,64] must share strides with unit inner stride")
+    if cache.dim() != 3 or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages, page_size, record_bytes]")
+    if not page_table.is_contiguous() or page_table.dim() != 2 or page_table.shape[0] != q_nope.shape[0]:
+        raise ValueError("page_table must be contiguous [B, max_pages]")
+    if seq_lens.numel() != q_nope.shape[0]:
+        raise ValueError("seq_lens must be [B]")
+
+
+def _workspace(B, H, max_splits, like, workspace):
+    need = decode_workspace_bytes(B, H, max_splits)
+    if need == 0:
+        return None
+    if workspace is None:
+        # zero-filled on first use; the kernels leave it reusable
+        workspace = torch.zeros(need, dtype=torch.uint8, device=like.device)
+    return workspace
+
+
+def decode(q_nope, q_rope, cache, page_table, seq_lens, outer_scale, softmax_scale, max_splits=1,
+           out=None, lse=None, workspace=None):
+    """Dense paged decode.  Returns (out fp32 [B,H,512], lse fp32 [B,H])."""
+    _decode_common(q_nope, q_rope, cache, page_table, seq_lens)
+    B, H = q_nope.shape[:2]
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=q_nope.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device) if lse is None else lse
+    ws = _workspace(B, H, max_splits, q_nope, workspace)
+    _check(lib().mla_decode_nvfp4(
+        q_nope.data_ptr(), q_rope.data_ptr(), q_nope.stride(0), q_nope.stride(1), cache.data_ptr(),
+        cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+        seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), int(max_splits), _ptr(ws),
+        0 if ws is None else ws.numel(), out.data_ptr(), lse.data_ptr(), _stream(q_nope)))
+    return out, lse
+
+
+def sparse_decode(q_nope, q_rope, cache, page_table, seq_lens, indices, outer_scale, softmax_scale,
+                  max_splits=1, out=None, lse=None, workspace=None):
+    """Top-k sparse paged decode.  indices int32 [B, topk]."""
+    _decode_common(q_nope, q_rope, cache, page_table, seq_lens)
+    _need(indices, torch.int32, "indices")
+    B, H = q_nope.shape[:2]
+    if not indices.is_contiguous() or indices.dim() != 2 or indices.shape[0] != B:
+        raise ValueError("indices must be contiguous [B, topk]")
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=q_nope.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device) if lse is None else lse
+    ws = _workspace(B, H, max_splits, q_nope, workspace)
+    _check(lib().mla_sparse_decode_nvfp4(
+        q_nope.data_ptr(), q_rope.data_ptr(), q_nope.stride(0), q_nope.stride(1), cache.data_ptr(),
+        cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+        seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), indices.data_ptr(),
+        indices.shape[1], int(max_splits), _ptr(ws), 0 if ws is None else ws.numel(), out.data_ptr(),
+        lse.data_ptr(), _stream(q_nope)))
+    return out, lse
+
+
+def lse_merge(partial_out, partial_lse, splits_per_seq=None, out=None, lse=None):
+    """partial_out fp32 [B,S,H,D], partial_lse fp32 [B,S,H] -> (out [B,H,D], lse [B,H])."""
+    _need(partial_out, torch.float32, "partial_out")
+    _need(partial_lse, torch.float32, "partial_lse")
+    if not partial_out.is_contiguous() or not partial_lse.is_contiguous():
+        raise ValueError("partials must be contiguous")
+    B, S, H, D = partial_out.shape
+    if tuple(partial_lse.shape) != (B, S, H):
+        raise ValueError("partial_lse must be [B, S, H]")
+    if splits_per_seq is not None:
+        _need(splits_per_seq, torch.int32, "splits_per_seq")
+    out = torch.empty((B, H, D), dtype=torch.float32, device=partial_out.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=partial_out.device) if lse is None else lse
+    _check(lib().mla_lse_merge(partial_out.data_ptr(), partial_lse.data_ptr(), _ptr(splits_per_seq), B, S, H,
+                               D, out.data_ptr(), lse.data_ptr(), _stream(partial_out)))
+    return out, lse
+
+
+def prefill(q, k, v, cu_seqlens, max_seqlen, softmax_scale, flags, g_q, g_k, g_v, g_p, out_global_scale,
+            with_lse=True, workspace=None):
+    """Varlen causal prefill with NVFP4 output.  Returns (codes uint8 [T,H,64],
+    swizzled scales uint8, lse fp32 [T,H] or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    T, H = q.shape[:2]
+    if q.shape[2] != 192 or k.shape != q.shape or v.shape != (T, H, 128) \
+            or q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("q, k [T,H,192] and v [T,H,128] with unit inner stride")
+    dev = q.device
+    codes = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    scales = torch.empty(max(1, swizzled_scale_bytes(T, H * 8)), dtype=torch.uint8, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if with_lse else None
+    need = prefill_workspace_bytes(T, H, flags)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().mla_prefill_nvfp4_out(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1), v.data_ptr(),
+        v.stride(0), v.stride(1), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), T, H,
+        float(softmax_scale), int(flags), float(g_q), float(g_k), float(g_v), float(g_p),
+        float(out_global_scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        codes.data_ptr(), scales.data_ptr(), _ptr(lse), _stream(q)))
+    return codes, scales, lse
+
+
+def quantize_rows(x, global_scale):
+    """x fp32 [M,K] contiguous -> (codes uint8 [M,K/2], swizzled scales uint8)."""
+    _need(x, torch.float32, "x")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be contiguous [M, K]")
+    M, K = x.shape
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(max(1, swizzled_scale_bytes(M, K // 16)), dtype=torch.uint8, device=x.device)
+    _check(lib().mla_nvfp4_quantize_rows(x.data_ptr(), M, K, float(global_scale), codes.data_ptr(),
+                                         scales.data_ptr(), _stream(x)))
+    return codes, scales

@@ -1,0 +1,351 @@
+// C ABI of libmla_nvfp4.so: argument validation, device check, launches.
+// The declarations, with the passages of the pages each call follows, are in
+// include/mla_nvfp4.h.  Validation order: pure host checks of the arguments,
+// then the no-op cases, then the device check, then the launches.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla_nvfp4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MLA_OK;
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    int state = (dev >= 0 && dev < kMaxDevices) ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(MLA_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        if (dev >= 0 && dev < kMaxDevices) g_arch_ok[dev].store(state, std::memory_order_relaxed);
+        if (state == 2)
+            return fail(MLA_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (state == 2) return fail(MLA_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    return MLA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int check_record(int record_bytes) {
+    if (record_bytes != MLA_RECORD_BYTES_BF16_ROPE && record_bytes != MLA_RECORD_BYTES_FP8_ROPE)
+        return fail(MLA_ERR_RECORD_BYTES, "NVFP4 MLA cache record must be 368 or 432 bytes, got %d",
+                    record_bytes);
+    return MLA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t decode_ws_out_bytes(int B, int H, int S) {
+    return align256((size_t)B * S * H * MLA_D_LATENT * sizeof(float));
+}
+
+// Common validation of dense and sparse decode arguments.
+int check_decode(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b, int64_t q_stride_h,
+                 const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                 const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
+                 float outer_scale, float softmax_scale, int max_splits, void* workspace,
+                 size_t workspace_bytes, float* out, float* lse) {
+    int rc = check_record(record_bytes);
+    if (rc) return rc;
+    if (B < 0 || B > 65535 || H < 1 || H > 4096)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= B <= 65535 and 1 <= H <= 4096 (B=%d H=%d)", B, H);
+    if (page_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "page_size must be >= 1 (got %d)", page_size);
+    if (max_pages_per_seq < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq must be >= 1");
+    if ((int64_t)max_pages_per_seq * page_size > INT32_MAX)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq * page_size exceeds int32");
+    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+    if (max_splits < 1 || max_splits > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "max_splits must be in [1, 65535]");
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+    if (!finite_pos(outer_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "outer_scale must be finite and > 0");
+    if (B > 0) {
+        if (!q_nope || !q_rope || !cache || !page_table || !seq_lens || !out || !lse)
+            return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+        if (q_stride_b % 8 || q_stride_h % 8 || !aligned(q_nope, 16) || !aligned(q_rope, 16))
+            return fail(MLA_ERR_INVALID_ARGUMENT, "q strides must be multiples of 8 elements and q 16-byte aligned");
+        if (!aligned(cache, 16) || !aligned(out, 16))
+            return fail(MLA_ERR_INVALID_ARGUMENT, "cache and out must be 16-byte aligned");
+        if (max_splits > 1) {
+            const size_t need = mla_decode_workspace_bytes(B, H, max_splits);
+            if (!workspace || workspace_bytes < need)
+                return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need,
+                            workspace_bytes);
+            if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+        }
+    }
+    return MLA_OK;
+}
+
+size_t decode_ws_lse_bytes(int B, int H, int S) { return align256((size_t)B * S * H * sizeof(float)); }
+int decode_count_stride(int H) { return (H + 15) / 16; }
+
+int run_decode(mla::DecodeArgs& a, void* workspace, hipStream_t stream) {
+    if (a.max_splits > 1) {
+        char* ws = static_cast<char*>(workspace);
+        a.ws_out = reinterpret_cast<float*>(ws);
+        a.ws_lse = reinterpret_cast<float*>(ws + decode_ws_out_bytes(a.B, a.H, a.max_splits));
+        a.ws_count = reinterpret_cast<int*>(ws + decode_ws_out_bytes(a.B, a.H, a.max_splits) +
+                                            decode_ws_lse_bytes(a.B, a.H, a.max_splits));
+    } else {
+        a.ws_out = nullptr;
+        a.ws_lse = nullptr;
+        a.ws_count = nullptr;
+    }
+    a.count_stride = decode_count_stride(a.H);
+    return hip_status(mla::launch_decode(a, stream), "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+int mla_nvfp4_record_bytes(int rope_fp8) {
+    return rope_fp8 ? MLA_RECORD_BYTES_FP8_ROPE : MLA_RECORD_BYTES_BF16_ROPE;
+}
+
+int mla_decode_num_splits(int seq_len, int max_splits) {
+    return mla::decode_num_splits(seq_len, max_splits < 1 ? 1 : max_splits);
+}
+
+size_t mla_decode_workspace_bytes(int B, int H, int max_splits) {
+    if (max_splits <= 1 || B <= 0 || H <= 0) return 0;
+    return decode_ws_out_bytes(B, H, max_splits) + decode_ws_lse_bytes(B, H, max_splits) +
+           align256((size_t)B * decode_count_stride(H) * sizeof(int));
+}
+
+size_t mla_nvfp4_swizzled_scale_bytes(int64_t rows, int64_t scale_cols) {
+    if (rows <= 0 || scale_cols <= 0) return 0;
+    return (size_t)((rows + 127) / 128 * 128) * (size_t)((scale_cols + 3) / 4 * 4);
+}
+
+int mla_nvfp4_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride, const uint16_t* k_pe,
+                          int64_t k_pe_row_stride, const int64_t* slot_mapping, int64_t T, uint8_t* cache,
+                          int64_t num_slots, int record_bytes, float outer_scale, void* stream) {
+    int rc = check_record(record_bytes);
+    if (rc) return rc;
+    if (T < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "T must be >= 0");
+    if (!finite_pos(outer_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "outer_scale must be finite and > 0");
+    if (num_slots < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_slots must be >= 0");
+    if (T > (int64_t)INT32_MAX * 4) return fail(MLA_ERR_INVALID_ARGUMENT, "T too large");
+    if (T == 0) return ok();
+    if (!kv_c || !k_pe || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (kv_c_row_stride % 8 || !aligned(kv_c, 16) || kv_c_row_stride < MLA_D_LATENT)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "kv_c rows must be 16-byte aligned with stride >= 512 (multiple of 8)");
+    if (k_pe_row_stride % 2 || !aligned(k_pe, 4) || k_pe_row_stride < MLA_D_ROPE)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "k_pe rows must be 4-byte aligned with stride >= 64 (even)");
+    if (!aligned(cache, 16)) return fail(MLA_ERR_INVALID_ARGUMENT, "cache must be 16-byte aligned");
+    rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_cache_write(kv_c, kv_c_row_stride, k_pe, k_pe_row_stride, slot_mapping, T,
+                                              cache, num_slots, record_bytes == MLA_RECORD_BYTES_FP8_ROPE,
+                                              outer_scale, static_cast<hipStream_t>(stream)),
+                      "cache write launch");
+}
+
+int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b, int64_t q_stride_h,
+                     const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                     const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
+                     float outer_scale, float softmax_scale, int max_splits, void* workspace,
+                     size_t workspace_bytes, float* out, float* lse, void* stream) {
+    int rc = check_decode(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                          page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                          workspace, workspace_bytes, out, lse);
+    if (rc) return rc;
+    if (B == 0) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    mla::DecodeArgs a{};
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.q_stride_b = q_stride_b;
+    a.q_stride_h = q_stride_h;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.record_bytes = record_bytes;
+    a.page_size = page_size;
+    a.page_table = page_table;
+    a.max_pages = max_pages_per_seq;
+    a.seq_lens = seq_lens;
+    a.indices = nullptr;
+    a.topk = 0;
+    a.B = B;
+    a.H = H;
+    a.outer_scale = outer_scale;
+    a.softmax_scale = softmax_scale;
+    a.max_splits = max_splits;
+    a.out = out;
+    a.lse = lse;
+    return run_decode(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b,
+                            int64_t q_stride_h, const uint8_t* cache, int64_t num_pages, int record_bytes,
+                            int page_size, const int32_t* page_table, int max_pages_per_seq,
+                            const int32_t* seq_lens, int B, int H, float outer_scale, float softmax_scale,
+                            const int32_t* indices, int topk, int max_splits, void* workspace,
+                            size_t workspace_bytes, float* out, float* lse, void* stream) {
+    int rc = check_decode(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                          page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                          workspace, workspace_bytes, out, lse);
+    if (rc) return rc;
+    if (topk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+    if (B > 0 && !indices) return fail(MLA_ERR_INVALID_ARGUMENT, "null indices");
+    if (B == 0) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    mla::DecodeArgs a{};
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.q_stride_b = q_stride_b;
+    a.q_stride_h = q_stride_h;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.record_bytes = record_bytes;
+    a.page_size = page_size;
+    a.page_table = page_table;
+    a.max_pages = max_pages_per_seq;
+    a.seq_lens = seq_lens;
+    a.indices = indices;
+    a.topk = topk;
+    a.B = B;
+    a.H = H;
+    a.outer_scale = outer_scale;
+    a.softmax_scale = softmax_scale;
+    a.max_splits = max_splits;
+    a.out = out;
+    a.lse = lse;
+    return run_decode(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+int mla_lse_merge(const float* partial_out, const float* partial_lse, const int32_t* splits_per_seq, int B, int S,
+                  int H, int D, float* out, float* lse, void* stream) {
+    if (B < 0 || S < 1 || H < 1 || D < 4 || D > 4096 || D % 4)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need B >= 0, S >= 1, H >= 1, D in [4, 4096] multiple of 4");
+    if (B == 0) return ok();
+    if (!partial_out || !partial_lse || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (!aligned(partial_out, 16) || !aligned(out, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "partial_out and out must be 16-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    mla::MergeArgs m{};
+    m.part_out = partial_out;
+    m.part_lse = partial_lse;
+    m.splits_per_seq = splits_per_seq;
+    m.B = B;
+    m.S = S;
+    m.H = H;
+    m.D = D;
+    m.out = out;
+    m.lse = lse;
+    return hip_status(mla::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+size_t mla_prefill_workspace_bytes(int64_t T, int H, unsigned qdq_flags) {
+    if (T <= 0 || H <= 0) return 0;
+    return mla::prefill_workspace_bytes(T, H, qdq_flags);
+}
+
+int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, const uint16_t* k,
+                          int64_t k_stride_t, int64_t k_stride_h, const uint16_t* v, int64_t v_stride_t,
+                          int64_t v_stride_h, const int32_t* cu_seqlens, int N, int max_seqlen, int64_t T, int H,
+                          float softmax_scale, unsigned qdq_flags, float g_q, float g_k, float g_v, float g_p,
+                          float out_global_scale, void* workspace, size_t workspace_bytes, uint8_t* out_fp4,
+                          uint8_t* out_scales, float* lse, void* stream) {
+    if (N < 0 || T < 0 || H < 1 || H > 1024 || max_seqlen < 0)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need N >= 0, T >= 0, 1 <= H <= 1024, max_seqlen >= 0");
+    if (qdq_flags & ~15u) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown qdq_flags bits 0x%x", qdq_flags);
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+    if (((qdq_flags & MLA_QDQ_Q) && !finite_pos(g_q)) || ((qdq_flags & MLA_QDQ_K) && !finite_pos(g_k)) ||
+        ((qdq_flags & MLA_QDQ_V) && !finite_pos(g_v)) || ((qdq_flags & MLA_QDQ_P) && !finite_pos(g_p)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "the scale of every enabled quantizer must be finite and > 0");
+    if (!finite_pos(out_global_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "out_global_scale must be finite and > 0");
+    if (T > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "T must fit in int32");
+    if (T == 0 || N == 0) return ok();
+    if (!q || !k || !v || !cu_seqlens || !out_fp4 || !out_scales)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (q_stride_t % 8 || q_stride_h % 8 || k_stride_t % 8 || k_stride_h % 8 || v_stride_t % 8 || v_stride_h % 8 ||
+        !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "q/k/v strides must be multiples of 8 elements and 16-byte aligned");
+    const size_t need = mla_prefill_workspace_bytes(T, H, qdq_flags);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need && !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    mla::PrefillArgs a{};
+    a.q = q; a.q_st = q_stride_t; a.q_sh = q_stride_h;
+    a.k = k; a.k_st = k_stride_t; a.k_sh = k_stride_h;
+    a.v = v; a.v_st = v_stride_t; a.v_sh = v_stride_h;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.max_seqlen = max_seqlen;
+    a.T = T;
+    a.H = H;
+    a.softmax_scale = softmax_scale;
+    a.flags = qdq_flags;
+    a.g_q = g_q; a.g_k = g_k; a.g_v = g_v; a.g_p = g_p; a.g_out = out_global_scale;
+    a.workspace = workspace;
+    a.out_fp4 = out_fp4;
+    a.out_scales = out_scales;
+    a.lse = lse;
+    hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(MLA_ERR_UNSUPPORTED, "prefill kernel not available");
+    return hip_status(e, "prefill launch");
+}
+
+int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale, uint8_t* codes,
+                            uint8_t* scales_swizzled, void* stream) {
+    if (M < 0 || K < 16 || K > 65536 || K % 16)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need M >= 0 and K in [16, 65536], a multiple of 16");
+    if (!finite_pos(global_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "global_scale must be finite and > 0");
+    if (M == 0) return ok();
+    if (!x || !codes || !scales_swizzled) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (!aligned(x, 16) || !aligned(codes, 8)) return fail(MLA_ERR_INVALID_ARGUMENT, "x must be 16-byte and codes 8-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_quantize_rows(x, M, K, global_scale, codes, scales_swizzled,
+                                                static_cast<hipStream_t>(stream)),
+                      "quantize_rows launch");
+}
+
+}  // extern "C"

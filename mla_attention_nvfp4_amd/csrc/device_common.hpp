@@ -1,0 +1,151 @@
+// Device helpers shared by the gfx950 kernels: NVFP4 element/scale codecs,
+// bf16 packing, MFMA operand types and wavefront reductions.
+//
+// Formats (public definitions; the pages only name them): e2m1 is the OCP MX
+// FP4 element (sign, 2-bit exponent with bias 1, 1-bit mantissa; magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6) and e4m3 the OCP FP8 E4M3FN scale (bias 7,
+// max 448, no infinities).  Encoders round to nearest, ties to even, and
+// saturate to the largest finite magnitude.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kQK = kLatent + kRope;  // 576
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- e4m3 --
+
+// e4m3 code of an fp32 value: RNE, satfinite (|t| >= 448 -> 0x7E), sign kept.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+    const uint32_t bits = f2u(t);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t a = bits & 0x7fffffffu;
+    uint32_t code;
+    if (a >= 0x43e00000u) {               // >= 448.0f (and inf)
+        code = 0x7eu;
+    } else if (a < 0x3c800000u) {         // < 2^-6: multiples of 2^-9
+        code = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);   // exact scaling, RNE
+    } else {                              // normal: round the mantissa to 3 bits
+        const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+        code = r - ((127u - 7u) << 3);
+    }
+    return sign | code;
+}
+
+// fp32 value of an e4m3 code (codes 0x7F/0xFF, NaN, are never produced by
+// the encoders here and are not special-cased).
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+    const uint32_t m = b & 0x7fu;
+    float v = (m >= 8u) ? u2f((m << 20) + (120u << 23))
+                        : (u2f((m << 20) + (121u << 23)) - 0.015625f);
+    return (b & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------- e2m1 --
+
+// e2m1 code of an fp32 value: RNE, saturating at 6, sign bit kept.  The code
+// of |q| counts the midpoints it passes; ties sit on the even side.
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+    const uint32_t s = (f2u(q) >> 28) & 8u;
+    const float a = __builtin_fabsf(q);
+    uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                 (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return s | m;
+}
+
+// Twice the magnitude of e2m1 code & 7, as 4-bit fields of one word.
+constexpr uint32_t kE2m1TwiceMag = 0xC8643210u;
+
+// fp32 value of an e2m1 code (bit 3 sign).
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+    const float mag = (float)((kE2m1TwiceMag >> ((c & 7u) * 4u)) & 0xfu) * 0.5f;
+    return (c & 8u) ? -mag : mag;
+}
+
+// Values of the two e2m1 codes in byte `sel` (0..3) of `w` (low nibble
+// first), by the gfx950 FP4 conversion with a unit scale (exact: checked
+// against e2m1_decode for all 256 bytes).
+template <int kSel>
+__device__ __forceinline__ f32x2 e2m1_pair(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);
+}
+
+// ------------------------------------------------------- NVFP4 blocks --
+
+// Two-level NVFP4 block scale for a block with amax `a` and dequant
+// multiplier g: t = a / (6 g), s = e4m3(t), d = s * g, inv = 1/d (0 when
+// d == 0); each step one IEEE fp32 operation (this file is compiled with
+// contraction off and correctly rounded division).
+struct Nvfp4Scale {
+    uint32_t code;
+    float inv;
+};
+
+__device__ __forceinline__ Nvfp4Scale nvfp4_block_scale(float a, float g) {
+    const float u = 6.0f * g;
+    const float t = a / u;
+    const uint32_t s = e4m3_encode(t);
+    const float d = e4m3_decode(s) * g;
+    return Nvfp4Scale{s, (d == 0.0f) ? 0.0f : 1.0f / d};
+}
+
+// Byte offset of scale (m, c) in the 128x4-swizzled layout with cpad
+// (a multiple of 4) scale columns: tiles of 128 rows x 4 columns (512 B),
+// row-tile major; inside a tile (m % 32) * 16 + ((m % 128) / 32) * 4 + c % 4.
+__device__ __forceinline__ int64_t swizzled_scale_offset(int64_t m, int64_t c, int64_t cpad) {
+    return ((m >> 7) * (cpad >> 2) + (c >> 2)) * 512 + (m & 31) * 16 + ((m & 127) >> 5) * 4 + (c & 3);
+}
+
+// ------------------------------------------------------------ bf16 pack --
+
+// Pack the bf16 numbers held exactly by two fp32 values (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+    return __builtin_amdgcn_perm(f2u(b), f2u(a), 0x07060302u);
+}
+
+// Round two fp32 values to bf16 (nearest even) and pack them (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    uint32_t ua = f2u(a), ub = f2u(b);
+    ua = (ua + 0x7fffu + ((ua >> 16) & 1u)) >> 16;
+    ub = (ub + 0x7fffu + ((ub >> 16) & 1u)) & 0xffff0000u;
+    return ua | ub;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xffff0000u); }
+
+// ----------------------------------------------------------------- MFMA --
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A (16x32) * B (32x16) + C, fp32 accumulate.  Lane l supplies row
+// l % 16 of A and column l % 16 of B, each with 8 consecutive k-slots
+// 8*(l/16) .. 8*(l/16)+7 (the same slots in A and B); it receives
+// D[4*(l/16) + i][l % 16] in element i.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ wavefront --
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_xor_sum(float v, int mask) {
+    return v + __shfl_xor(v, mask, 64);
+}
+
+}  // namespace mla

@@ -29,3 +29,21 @@ def golden_rows(name):
             if line and not line.startswith("#"):
                 rows.append(line)
     return rows
+
+
+_WORKLOADS = {}
+
+
+@pytest.fixture(scope="session")
+def decode_workload():
+    """Cached seeded decode workloads (generation of the big ones takes a while)."""
+    from mla_attention_nvfp4_amd import workloads
+
+    def get(n, H=None):
+        key = (n, H)
+        if key not in _WORKLOADS:
+            print(f"  generating decode workload {n} (H={H})", flush=True)
+            _WORKLOADS[key] = workloads.decode_workload(n, H)
+        return _WORKLOADS[key]
+
+    return get

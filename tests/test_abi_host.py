@@ -1,0 +1,88 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_attention_nvfp4_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_nvfp4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_constants_and_policy():
+    assert L.record_bytes(False) == 432 and L.record_bytes(True) == 368
+    assert L.decode_num_splits(4096, 4) == 4
+    assert L.decode_num_splits(0, 8) == 1 and L.decode_num_splits(1, 8) == 1
+    assert L.decode_num_splits(257, 8) == 2
+    for n in (1, 63, 64, 65, 300, 1000, 4096, 32768):
+        for s in (1, 2, 3, 4, 8, 32):
+            k = L.decode_num_splits(n, s)
+            tiles = (n + 63) // 64
+            assert 1 <= k <= s and k <= tiles
+    assert L.decode_workspace_bytes(64, 128, 4) == 64 * 4 * 128 * 512 * 4 + 64 * 4 * 128 * 4 + 64 * 8 * 4
+    assert L.decode_workspace_bytes(64, 128, 1) == 0
+    assert L.swizzled_scale_bytes(1, 1) == 128 * 4
+    assert L.swizzled_scale_bytes(129, 1024) == 256 * 1024
+
+
+def _decode_args(**kw):
+    a = dict(q_nope=1 << 20, q_rope=1 << 20, sb=576 * 128, sh=576, cache=1 << 20, num_pages=4,
+             rec=432, page=64, pt=1 << 20, maxp=4, seq=1 << 20, B=1, H=16, outer=1.0, scale=0.04,
+             splits=1, ws=None, wsb=0, out=1 << 20, lse=1 << 20, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("q_nope", "q_rope", "sb", "sh", "cache", "num_pages", "rec", "page", "pt", "maxp",
+                           "seq", "B", "H", "outer", "scale", "splits", "ws", "wsb", "out", "lse", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rec=400), -2), (dict(rec=0), -2), (dict(rec=431), -2),
+    (dict(H=0), -1), (dict(page=0), -1), (dict(splits=0), -1),
+    (dict(outer=0.0), -1), (dict(outer=float("inf")), -1), (dict(outer=float("nan")), -1),
+    (dict(scale=-1.0), -1), (dict(scale=float("nan")), -1), (dict(sb=576 * 128 + 1), -1),
+    (dict(q_nope=None), -1), (dict(num_pages=0), -1),
+    (dict(splits=4), -4), (dict(splits=4, ws=1 << 20, wsb=100), -4),
+])
+def test_decode_rejects_invalid_arguments(kw, code):
+    lib = L.lib()
+    assert lib.mla_decode_nvfp4(*_decode_args(**kw)) == code
+    assert lib.mla_last_error()
+
+
+def test_other_entry_points_reject_invalid_arguments():
+    lib = L.lib()
+    # cache write: bad record width, bad scale, misaligned rows
+    assert lib.mla_nvfp4_cache_write(1 << 20, 576, 1 << 20, 576, 1 << 20, 5, 1 << 20, 10, 400, 1.0, None) == -2
+    assert lib.mla_nvfp4_cache_write(1 << 20, 576, 1 << 20, 576, 1 << 20, 5, 1 << 20, 10, 432, -1.0, None) == -1
+    assert lib.mla_nvfp4_cache_write(1 << 20, 577, 1 << 20, 576, 1 << 20, 5, 1 << 20, 10, 432, 1.0, None) == -1
+    assert lib.mla_nvfp4_cache_write(None, 576, None, 576, None, 0, None, 0, 432, 1.0, None) == 0  # T = 0
+    # sparse: topk must be positive
+    args = _decode_args()
+    assert lib.mla_sparse_decode_nvfp4(*args[:15], 1 << 20, 0, 1, None, 0, 1 << 20, 1 << 20, None) == -1
+    # merge: D must be a multiple of 4
+    assert lib.mla_lse_merge(1 << 20, 1 << 20, None, 1, 2, 1, 6, 1 << 20, 1 << 20, None) == -1
+    # prefill: unknown flag bits, bad scales
+    pf = [1 << 20, 192 * 4, 192, 1 << 20, 192 * 4, 192, 1 << 20, 128 * 4, 128, 1 << 20, 1, 10, 10, 4, 0.07]
+    assert lib.mla_prefill_nvfp4_out(*pf, 16, 1., 1., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -1
+    assert lib.mla_prefill_nvfp4_out(*pf, 15, 1., 0., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -1
+    assert lib.mla_prefill_nvfp4_out(*pf, 15, 1., 1., 1., 1., 0., None, 0, 1 << 20, 1 << 20, None, None) == -1
+    # quantize_rows: K must be a multiple of 16
+    assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 24, 1.0, 1 << 20, 1 << 20, None) == -1
+    assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 32, 0.0, 1 << 20, 1 << 20, None) == -1

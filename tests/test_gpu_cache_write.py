@@ -1,0 +1,65 @@
+"""GPU parity: the cache-write kernel against the oracle, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import bits, gpu_cache
+from mla_attention_nvfp4_amd import ops, workloads
+from oracle import record as OR
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_records(inp, cache, rows):
+    flat = cache.view(-1, inp.record_bytes)
+    slots = inp.slot_mapping[rows]
+    got = flat[slots.cuda()].cpu().numpy()
+    want = OR.pack_records(bits(inp.kv_c[rows]), bits(inp.k_pe[rows]), inp.outer_scale, inp.record_bytes)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at (row, byte) {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("rec", [432, 368])
+@pytest.mark.parametrize("outer", [1.0, 0.6180339887, 1.9])
+def test_small_records_bit_exact(rec, outer):
+    inp = workloads.small_decode(100 + rec, 3, 16, [70, 1, 129], page_size=16, rec=rec, outer=outer,
+                                 outliers=True)
+    cache = gpu_cache(inp, fill=0xAB)
+    _check_records(inp, cache, np.arange(inp.kv_c.shape[0]))
+
+
+def test_skipped_slots_leave_cache_untouched():
+    inp = workloads.small_decode(7, 2, 16, [40, 40], page_size=16, rec=432)
+    T = inp.kv_c.shape[0]
+    slots = inp.slot_mapping.clone()
+    slots[3] = -1
+    slots[10] = 10 ** 9          # beyond the cache: skipped by the kernel
+    slots[11] = -77
+    cache = torch.full((inp.num_pages, inp.page_size, inp.record_bytes), 0xAB, dtype=torch.uint8, device="cuda")
+    ops.cache_write(inp.kv_c.cuda(), inp.k_pe.cuda(), slots.cuda(), cache, inp.outer_scale)
+    flat = cache.view(-1, 432).cpu().numpy()
+    want = np.full_like(flat, 0xAB)
+    keep = slots >= 0
+    keep &= slots < flat.shape[0]
+    OR.cache_write(want, bits(inp.kv_c), bits(inp.k_pe), np.where(keep.numpy(), slots.numpy(), -1),
+                   inp.outer_scale)
+    assert np.array_equal(flat, want)
+
+
+def test_strided_inputs():
+    """kv_c and k_pe as column slices of one [T, 576] tensor."""
+    inp = workloads.small_decode(8, 1, 16, [100], page_size=64, rec=368, outer=0.75)
+    both = torch.cat([inp.kv_c, inp.k_pe], dim=1).cuda()
+    cache = torch.zeros((inp.num_pages, 64, 368), dtype=torch.uint8, device="cuda")
+    ops.cache_write(both[:, :512], both[:, 512:], inp.slot_mapping.cuda(), cache, inp.outer_scale)
+    _check_records(inp, cache, np.arange(100))
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3])
+def test_workload_records_bit_exact(n, decode_workload):
+    inp = decode_workload(n)
+    cache = gpu_cache(inp)
+    T = inp.kv_c.shape[0]
+    rows = np.arange(T) if n == 0 else np.random.default_rng(n).choice(T, 1024, replace=False)
+    print(f"  workload {n}: T={T}, checking {len(rows)} records", flush=True)
+    _check_records(inp, cache, np.sort(rows))

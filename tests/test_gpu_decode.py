@@ -1,0 +1,145 @@
+"""GPU parity: dense and sparse paged decode and the LSE merge against the
+oracle, on small ragged cases, edge cases and the full workload sizes."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import compare, gpu_cache, gpu_decode, oracle_decode
+from mla_attention_nvfp4_amd import ops, workloads
+from oracle import decode as OD
+
+pytestmark = pytest.mark.gpu
+
+SMALL_DENSE = [
+    # seed, B, H, lens, page, rec, outer, splits
+    (1, 3, 16, [0, 1, 65], 64, 432, 1.0, 1),
+    (2, 4, 20, [63, 64, 130, 300], 16, 368, 0.75, 3),
+    (3, 2, 128, [1000, 513], 64, 432, 1.7, 4),
+    (4, 5, 32, [5, 200, 129, 64, 1], 48, 432, 0.55, 2),
+    (5, 2, 64, [2049, 4096], 64, 368, 1.3, 16),
+    (6, 1, 1, [77], 8, 432, 1.0, 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_DENSE, ids=[f"dense{c[0]}" for c in SMALL_DENSE])
+def test_dense_small(case):
+    seed, B, H, lens, page, rec, outer, splits = case
+    inp = workloads.small_decode(seed, B, H, lens, page_size=page, rec=rec, outer=outer,
+                                 max_splits=splits, outliers=(seed % 2 == 0))
+    print(f"  dense seed={seed} B={B} H={H} lens={lens} page={page} rec={rec} splits={splits}", flush=True)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, list(range(B)))
+    compare(out, lse, ref_out, ref_lse, list(range(B)), f"dense{seed}")
+
+
+SMALL_SPARSE = [
+    # seed, B, H, lens, topk, invalid_frac, splits
+    (11, 3, 16, [100, 0, 700], 96, 0.1, 1),
+    (12, 3, 16, [100, 5, 700], 96, 0.1, 2),
+    (13, 2, 128, [5000, 3000], 512, 0.1, 4),
+    (14, 2, 48, [64, 300], 130, 0.5, 3),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_SPARSE, ids=[f"sparse{c[0]}" for c in SMALL_SPARSE])
+def test_sparse_small(case):
+    seed, B, H, lens, topk, bad, splits = case
+    inp = workloads.small_decode(seed, B, H, lens, page_size=64, rec=432, outer=1.2, max_splits=splits,
+                                 topk=topk, invalid_frac=bad)
+    print(f"  sparse seed={seed} B={B} H={H} lens={lens} topk={topk} splits={splits}", flush=True)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, list(range(B)))
+    compare(out, lse, ref_out, ref_lse, list(range(B)), f"sparse{seed}")
+
+
+def test_sparse_all_masked_and_masked_pages():
+    inp = workloads.small_decode(21, 2, 16, [200, 200], page_size=64, rec=432, topk=64)
+    inp.indices[0] = -1                       # nothing valid for sequence 0
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    ref_out, ref_lse = oracle_decode(inp, [1])
+    compare(out, lse, ref_out, ref_lse, [1], "sparse-masked")
+
+
+def test_out_of_range_page_ids_are_masked():
+    """A page id outside the cache masks its tokens instead of being read."""
+    inp = workloads.small_decode(22, 1, 16, [192], page_size=64, rec=432)
+    cache = gpu_cache(inp)
+    pt = inp.page_table.clone()
+    pt[0, 1] = 10 ** 6
+    q = inp.q.cuda()
+    out, lse = ops.decode(q[..., :512], q[..., 512:], cache, pt.cuda(), inp.seq_lens.cuda(),
+                          inp.outer_scale, inp.softmax_scale, 1)
+    # reference: the same sequence without its second page
+    flat = torch.cat([cache.view(-1, 432)[inp.slot_mapping[:64].cuda()],
+                      cache.view(-1, 432)[inp.slot_mapping[128:].cuda()]]).view(2, 64, 432)
+    out2, lse2 = ops.decode(q[..., :512], q[..., 512:], flat.contiguous(),
+                            torch.tensor([[0, 1]], dtype=torch.int32, device="cuda"),
+                            torch.tensor([128], dtype=torch.int32, device="cuda"),
+                            inp.outer_scale, inp.softmax_scale, 1)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, out2, rtol=1e-5, atol=1e-6) and torch.allclose(lse, lse2, atol=1e-5)
+
+
+def test_split_counts_agree_and_runs_are_deterministic():
+    inp = workloads.small_decode(31, 3, 128, [4096, 1500, 300], page_size=64, rec=432, outer=0.9)
+    cache = gpu_cache(inp)
+    ref_out, ref_lse = oracle_decode(inp, [0, 1, 2])
+    base = None
+    for splits in (1, 2, 4, 7, 16):
+        out, lse = gpu_decode(inp, cache, max_splits=splits)
+        compare(out, lse, ref_out, ref_lse, [0, 1, 2], f"splits={splits}")
+        out2, lse2 = gpu_decode(inp, cache, max_splits=splits)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2), "not bitwise deterministic"
+        if base is None:
+            base = out
+
+
+def test_lse_merge_kernel():
+    rng = np.random.default_rng(40)
+    B, S, H, D = 5, 6, 7, 512
+    po = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    pl = rng.standard_normal((B, S, H)).astype(np.float32) * 3
+    pl[0, 2] = -np.inf
+    pl[1] = -np.inf                           # all empty
+    pl[2, :, 3] = -np.inf
+    counts = np.array([6, 6, 3, 0, 1], np.int32)
+    out, lse = ops.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                             torch.from_numpy(counts).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    for b in range(B):
+        n = counts[b]
+        if n == 0:
+            ro, rl = np.zeros((H, D)), np.full(H, -np.inf)
+        else:
+            ro, rl = OD.lse_merge(po[b, :n], pl[b, :n])
+        assert np.array_equal(np.isneginf(lse[b]), np.isneginf(rl))
+        fin = ~np.isneginf(rl)
+        assert np.allclose(out[b], ro, rtol=1e-5, atol=1e-6)
+        assert np.allclose(lse[b][fin], rl[fin], rtol=0, atol=1e-5)
+    # no count array: all S splits
+    out, lse = ops.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ro, rl = OD.lse_merge(po[3], pl[3])
+    assert np.allclose(out.cpu().numpy()[3], ro, rtol=1e-5, atol=1e-6)
+
+
+FULL = [(0, None), (1, None), (1, 16), (2, None), (3, None)]
+
+
+@pytest.mark.parametrize("n,H", FULL, ids=[f"workload{n}" + (f"-H{H}" if H else "") for n, H in FULL])
+def test_workload_full_size(n, H, decode_workload):
+    """Full workload sizes in the launch configuration the benchmark times;
+    the oracle checks a subset of sequences (all heads)."""
+    inp = decode_workload(n, H)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    batch = {0: [0], 1: [0, 1], 2: [0, 1, 2, 3], 3: [0, 1, 2, 3]}[n]
+    ref_out, ref_lse = oracle_decode(inp, batch)
+    compare(out, lse, ref_out, ref_lse, batch, f"workload{n} H={inp.H}")
+    # every sequence, including those the oracle skipped, must be finite
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
