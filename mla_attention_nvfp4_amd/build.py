@@ -29,13 +29,19 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  decode.hip: MFMA accumulators in VGPRs, so the
+# (rare) softmax rescale of the output accumulators needs no AGPR round trip
+# and the loop-carried accumulators are not copied between register files.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

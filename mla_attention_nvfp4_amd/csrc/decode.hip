@@ -8,26 +8,32 @@
 // the per-layer outer scale on read; review 2: Q is staged as bf16 with no
 // Q quantization.
 //
-// Work item: workgroup (split s, sequence b, head group hg) with NW
-// wavefronts, wavefront w owning 16 query heads.  The token range of the
-// split is walked in tiles of 64 tokens:
-//   phase A  every thread dequantizes an 8-token x 8-element block of the
-//            latent (e2m1 code x e4m3 scale, exact in bf16; the outer scale
-//            is NOT folded in) and writes it twice to LDS: token-major (Ks,
-//            the QK^T operand) and element-major (Vt, the PV operand); the
-//            RoPE part goes to Ks columns 512..575.  The global loads of the
-//            next tile are issued before the MMA phase of this one.
-//   phase B  each wavefront: S^T = K Q^T with v_mfma_f32_16x16x32_bf16
-//            (A = Ks rows from LDS, B = the wave's 16 Q rows held in VGPRs),
-//            two accumulators (latent and RoPE) so that
-//            z = scale * (outer * s_nope + s_rope) in fp32; online softmax
-//            in base 2; P, split into bf16 hi + lo parts, stays in
-//            registers as the B operand of O^T = V^T P^T (A = Vt rows from
-//            LDS, each fragment used by two MFMAs).
+// Work item: workgroup (split s, sequence b, head group hg) of NW
+// wavefronts, each owning 16 query heads.  The split's tokens are walked in
+// tiles of 32, software-pipelined:
+//   offsets   record byte offsets (page-table walk) of tile t+3 into a ring
+//             of 4 LDS slots (the position / index load one iteration
+//             earlier than the page-table load, so no load is waited for
+//             right after it is issued);
+//   staging   each wavefront loads its own 32/NW records of tile t+2 into
+//             registers (coalesced runs per record; no cross-wave traffic);
+//   dequant   each wavefront dequantizes its own records of tile t+1 into
+//             the free token-major tile (e2m1 code x e4m3 scale is exact in
+//             bf16; the outer scale is not folded), RoPE in columns
+//             512..575;
+//   compute   tile t: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = tile
+//             rows, B = the wavefront's Q rows in registers); the latent
+//             part of the accumulator is multiplied by the outer scale
+//             before the RoPE k-steps; online softmax in base 2 with lazy
+//             rescaling; P split into bf16 hi + lo parts (B operand) for
+//             O^T = V^T P^T, whose A operand is read from the same
+//             token-major tile with the transposing LDS load
+//             ds_read_b64_tr_b16 (V is the latent).
 // The epilogue writes out = outer * O / l and lse = m + ln l (natural log)
 // to the output when the sequence has one split; otherwise it writes the
 // partial to the workspace and the last workgroup of the sequence and head
-// group to finish merges the partials (same rule as lse_merge_kernel).
+// group to finish merges the partials in split order (same rule as
+// lse_merge_kernel), then resets the arrival counter.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -35,26 +41,28 @@ namespace mla {
 
 namespace {
 
-constexpr int kTile = 64;            // tokens per tile
-constexpr int kKsPitch = kQK + 8;    // bf16 elements per Ks row (584)
-constexpr int kVtPitch = kTile + 8;  // bf16 elements per Vt row (72)
+constexpr int kTile = 32;            // tokens per tile
+constexpr int kKsPitch = kQK + 16;   // bf16 elements per tile row (592: 1184 B, conflict-free)
+constexpr int kRing = 4;             // offset ring slots
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 struct DecodeSmem {
-    uint16_t ks[kTile * kKsPitch];        // [token][576 (+8)]  74752 B
-    uint16_t vt[kLatent * kVtPitch];      // [element][64 (+8)] 73728 B
-    int64_t offs[2][kTile];               // record byte offset, -1 = masked
+    uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
+    int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
     int last;                             // this workgroup merges the splits
 };
 
+
 template <int NW, bool kRopeFp8, bool kSparse>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void decode_kernel(DecodeArgs p) {
     constexpr int kRec = kRopeFp8 ? 368 : 432;
-    constexpr int kG = 8 / NW;            // 8-token groups per thread
-    constexpr int kR = 512 / (64 * NW);   // RoPE 16-byte units per thread
+    constexpr int kRpw = kTile / NW;                         // records per wavefront
     __shared__ DecodeSmem sm;
 
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
@@ -67,21 +75,20 @@ void decode_kernel(DecodeArgs p) {
     const int n_items = kSparse ? p.topk : L;
     const int ns = decode_num_splits(n_items, p.max_splits);
     if (s >= ns) return;
-    const int ct = decode_chunk_tiles(n_items, p.max_splits);
-    const int nt = (n_items + kTile - 1) / kTile;
-    const int t_begin = s * ct;
-    const int t_end = min(nt, t_begin + ct);
+    const int ct = decode_chunk_tiles(n_items, p.max_splits);  // in 64-token tiles
+    const int T0 = 2 * s * ct;
+    const int T1 = min((n_items + kTile - 1) / kTile, T0 + 2 * ct);
 
-    const int h_base = hg * 16 * NW + 16 * w;
+    const int h_base = hg * (16 * NW) + 16 * w;
     const bool wave_active = h_base < p.H;
     const int hq = h_base + c16;
 
     // Q as the B operand of S^T = K Q^T: k-step kk covers d = 32kk..32kk+31.
     bf16x8 qf[18];
     {
-        const u32x4 zero = {0u, 0u, 0u, 0u};
         const bool ok = hq < p.H;
-        const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)hq * p.q_stride_h + 8 * gq;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(ok ? hq : 0) * p.q_stride_h + 8 * gq;
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk)
             qf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero);
@@ -94,251 +101,251 @@ void decode_kernel(DecodeArgs p) {
     const float scale_log2 = p.softmax_scale * kLog2e;
     const float outer = p.outer_scale;
 
-    auto compute_offs = [&](int t, int buf) {
-        // threads 0..63: record offset of the tile's tokens
-        const int item = t * kTile + tid;
-        int64_t off = -1;
-        if (item < n_items) {
-            const int pos = kSparse ? p.indices[(int64_t)b * p.topk + item] : item;
-            if (pos >= 0 && pos < L) {
-                const int pg = p.page_table[(int64_t)b * p.max_pages + pos / p.page_size];
-                if (pg >= 0 && pg < p.num_pages)
-                    off = ((int64_t)pg * p.page_size + pos % p.page_size) * kRec;
-            }
-        }
-        sm.offs[buf][tid] = off;
+    // ---- offsets.  Loads are issued by every lane of wavefront 0 from
+    // clamped (always valid) addresses and masked afterwards, so the
+    // control flow stays uniform and the compiler's load counters exact.
+    auto position_of = [&](int t) -> int {
+        const int item = t * kTile + (lane & (kTile - 1));
+        const int ic = min(item, max(n_items - 1, 0));
+        const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
+        return (item < n_items && pos >= 0 && pos < L) ? pos : -1;
+    };
+    auto page_of = [&](int pos) -> int {
+        const int pi = pos < 0 ? 0 : pos / p.page_size;
+        return p.page_table[(int64_t)b * p.max_pages + pi];
+    };
+    auto offset_of = [&](int pos, int pg) -> int64_t {
+        return (pos >= 0 && pg >= 0 && pg < p.num_pages)
+                   ? ((int64_t)pg * p.page_size + pos % p.page_size) * kRec : int64_t(-1);
+    };
+    auto compute_offs = [&](int t, int slot) {
+        const int pos = position_of(t);
+        const int64_t off = offset_of(pos, page_of(pos));
+        if (lane < kTile) sm.offs[slot][lane] = off;
     };
 
-    // per-thread staging registers for one tile
-    uint32_t codes[kG][8], scl[kG][8];
-    u32x4 rope[kR];
-
-    // Masked tokens load record 0 (always present) and are zeroed, so the
-    // loads need no branches.
-    auto load_tile = [&](int buf) {
+    // ---- staging: this wavefront's records kRpw*w .. +kRpw-1 of a tile in
+    // registers.  Lane l holds code word l (elements 8l..8l+7) and the
+    // matching scale byte of each record, plus one 16-byte RoPE unit
+    // (record l/8, unit l%8); every load is a contiguous run per record.
+    // Masked tokens load record 0 (always present) and are zeroed.
+    uint32_t rc[kRpw], rs[kRpw];
+    u32x4 rr;
+    // (the loaded words are used as they are; masking happens in dequant,
+    // one iteration later, so that no load is waited for here)
+    auto load_raw = [&](int slot) {
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int chunk = 8 * (w * kG + g) + (lane & 7);
-            const int tg = lane >> 3;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int64_t off = sm.offs[buf][tg * 8 + r];
-                const uint8_t* rp = cache + (off < 0 ? 0 : off);
-                const uint32_t cw = *reinterpret_cast<const uint32_t*>(rp + 4 * chunk);
-                const uint32_t sw = rp[256 + (chunk >> 1)];
-                codes[g][r] = off < 0 ? 0u : cw;
-                scl[g][r] = off < 0 ? 0u : sw;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kR; ++i) {
-            const int item = tid + i * NW * 64;
-            const int64_t off = sm.offs[buf][item >> 3];
+        for (int r = 0; r < kRpw; ++r) {
+            const int64_t off = sm.offs[slot][kRpw * w + r];
             const uint8_t* rp = cache + (off < 0 ? 0 : off);
-            const int u = item & 7;
-            u32x4 v;
-            if (kRopeFp8) {
-                const u32x2 v2 = *reinterpret_cast<const u32x2*>(rp + 288 + 8 * u);
-                v = u32x4{v2[0], v2[1], 0u, 0u};
-            } else {
-                v = *reinterpret_cast<const u32x4*>(rp + 288 + 16 * u);
-            }
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            rope[i] = off < 0 ? zero : v;
+            rc[r] = *reinterpret_cast<const uint32_t*>(rp + 4 * lane);
+            rs[r] = rp[256 + (lane >> 1)];
+        }
+        const int r = (lane >> 3) % kRpw, u = lane & 7;
+        const int64_t off = sm.offs[slot][kRpw * w + r];
+        const uint8_t* rp = cache + (off < 0 ? 0 : off);
+        if (kRopeFp8) {
+            const u32x2 v2 = *reinterpret_cast<const u32x2*>(rp + 288 + 8 * u);
+            rr = u32x4{v2[0], v2[1], 0u, 0u};
+        } else {
+            rr = *reinterpret_cast<const u32x4*>(rp + 288 + 16 * u);
         }
     };
 
-    auto dequant_tile = [&]() {
+    // ---- dequant of the staged records into tile rows kRpw*w + r:
+    // lane = 16-byte column chunk (8 latent elements)
+    auto dequant = [&](int kbuf, int slot) {
+        uint16_t* ks = sm.ks[kbuf];
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int chunk = 8 * (w * kG + g) + (lane & 7);
-            const int tg = lane >> 3;
-            // kw[r][j]: bf16 pair (elements 2j, 2j+1) of token row r
-            uint32_t kw[8][4];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float sc = e4m3_decode(scl[g][r]);
-                const uint32_t c = codes[g][r];
-                {
-                    const f32x2 v0 = e2m1_pair<0>(c), v1 = e2m1_pair<1>(c);
-                    const f32x2 v2 = e2m1_pair<2>(c), v3 = e2m1_pair<3>(c);
-                    kw[r][0] = pack_bf16_exact(v0[0] * sc, v0[1] * sc);
-                    kw[r][1] = pack_bf16_exact(v1[0] * sc, v1[1] * sc);
-                    kw[r][2] = pack_bf16_exact(v2[0] * sc, v2[1] * sc);
-                    kw[r][3] = pack_bf16_exact(v3[0] * sc, v3[1] * sc);
-                }
-                const u32x4 wv = {kw[r][0], kw[r][1], kw[r][2], kw[r][3]};
-                *reinterpret_cast<u32x4*>(&sm.ks[(tg * 8 + r) * kKsPitch + 8 * chunk]) = wv;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // element e of rows (2i, 2i+1): low or high halves of kw[.][e/2]
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 wv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    wv[i] = __builtin_amdgcn_perm(kw[2 * i + 1][e >> 1], kw[2 * i][e >> 1], sel);
-                *reinterpret_cast<u32x4*>(&sm.vt[(8 * chunk + e) * kVtPitch + 8 * tg]) = wv;
-            }
+        for (int r = 0; r < kRpw; ++r) {
+            const int tok = kRpw * w + r;
+            const bool valid = sm.offs[slot][tok] >= 0;
+            const uint32_t c = valid ? rc[r] : 0u;
+            const float sc = e4m3_decode(valid ? rs[r] : 0u);
+            const f32x2 v0 = e2m1_pair<0>(c), v1 = e2m1_pair<1>(c);
+            const f32x2 v2 = e2m1_pair<2>(c), v3 = e2m1_pair<3>(c);
+            const u32x4 wv = {pack_bf16_exact(v0[0] * sc, v0[1] * sc), pack_bf16_exact(v1[0] * sc, v1[1] * sc),
+                              pack_bf16_exact(v2[0] * sc, v2[1] * sc), pack_bf16_exact(v3[0] * sc, v3[1] * sc)};
+            *reinterpret_cast<u32x4*>(&ks[tok * kKsPitch + 8 * lane]) = wv;
         }
-#pragma unroll
-        for (int i = 0; i < kR; ++i) {
-            const int item = tid + i * NW * 64;
-            const int tok = item >> 3, u = item & 7;
+        // RoPE: kRpw tokens x 8 units of 8 elements
+        if (lane < 8 * kRpw) {
+            const int tok = kRpw * w + (lane >> 3), u = lane & 7;
+            const bool valid = sm.offs[slot][tok] >= 0;
             u32x4 wv;
             if (kRopeFp8) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const uint32_t x = rope[i][j];
+                    const uint32_t x = rr[j];
                     wv[2 * j] = pack_bf16_exact(e4m3_decode(x & 0xffu), e4m3_decode((x >> 8) & 0xffu));
                     wv[2 * j + 1] = pack_bf16_exact(e4m3_decode((x >> 16) & 0xffu), e4m3_decode(x >> 24));
                 }
             } else {
-                wv = rope[i];
+                wv = rr;
             }
-            *reinterpret_cast<u32x4*>(&sm.ks[tok * kKsPitch + kLatent + 8 * u]) = wv;
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(&ks[tok * kKsPitch + kLatent + 8 * u]) = valid ? wv : zero;
         }
     };
 
     f32x4 o[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    auto mma_tile = [&](int buf) {
-        f32x4 sn[4], sr[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            sn[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            sr[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // A fragments double-buffered one k-step ahead; the scheduling
-        // barrier keeps the compiler from hoisting every LDS read at once.
+    auto compute = [&](int kbuf, int slot) {
+        const uint16_t* ks = sm.ks[kbuf];
+        // S^T accumulators: latent k-steps alternate between two sets so
+        // consecutive MFMAs are independent; the latent part is multiplied
+        // by the outer scale before the RoPE k-steps are added.
+        f32x4 sa[2], sb[2];
+        sa[0] = sa[1] = sb[0] = sb[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto ks_frag = [&](int kk, int tt) {
-            return *reinterpret_cast<const u32x4*>(&sm.ks[(16 * tt + c16) * kKsPitch + 32 * kk + 8 * gq]);
+            return *reinterpret_cast<const u32x4*>(&ks[(16 * tt + c16) * kKsPitch + 32 * kk + 8 * gq]);
         };
-        u32x4 acur[4], anxt[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acur[tt] = ks_frag(0, tt);
+        // fragments two k-steps ahead of their MFMAs
+        u32x4 f0[3], f1[3];
+        f0[0] = ks_frag(0, 0);
+        f1[0] = ks_frag(0, 1);
+        f0[1] = ks_frag(1, 0);
+        f1[1] = ks_frag(1, 1);
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) {
-            if (kk + 1 < 18) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) anxt[tt] = ks_frag(kk + 1, tt);
+            if (kk + 2 < 18) {
+                f0[(kk + 2) % 3] = ks_frag(kk + 2, 0);
+                f1[(kk + 2) % 3] = ks_frag(kk + 2, 1);
             }
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                if (kk < 16) sn[tt] = mfma16x16x32(as_bf16x8(acur[tt]), qf[kk], sn[tt]);
-                else sr[tt] = mfma16x16x32(as_bf16x8(acur[tt]), qf[kk], sr[tt]);
+            const u32x4 a0 = f0[kk % 3], a1 = f1[kk % 3];
+            if (kk < 16 && (kk & 1)) {
+                sb[0] = mfma16x16x32(as_bf16x8(a0), qf[kk], sb[0]);
+                sb[1] = mfma16x16x32(as_bf16x8(a1), qf[kk], sb[1]);
+            } else {
+                sa[0] = mfma16x16x32(as_bf16x8(a0), qf[kk], sa[0]);
+                sa[1] = mfma16x16x32(as_bf16x8(a1), qf[kk], sa[1]);
+            }
+            if (kk == 15) {
+                sa[0] = (sa[0] + sb[0]) * outer;
+                sa[1] = (sa[1] + sb[1]) * outer;
             }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) acur[tt] = anxt[tt];
         }
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
-        float z[4][4];
+        float z[2][4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = sm.offs[buf][16 * tt + 4 * gq + i] >= 0;
-                const float v = scale_log2 * (outer * sn[tt][i] + sr[tt][i]);
-                z[tt][i] = valid ? v : -INFINITY;
+                const bool valid = sm.offs[slot][16 * tt + 4 * gq + i] >= 0;
+                z[tt][i] = valid ? scale_log2 * sa[tt][i] : -INFINITY;
                 mx = fmaxf(mx, z[tt][i]);
             }
-        }
         mx = wave_xor_max(mx, 16);
         mx = wave_xor_max(mx, 32);
-        // Lazy rescaling: the reference max m_run moves only when a score
-        // exceeds it by more than kRescaleSlack (log2 units), so p <= 2^8 and
-        // O is rescaled rarely (a rescale costs AGPR round trips).  The result
-        // is the same softmax; only rounding differs.
+        // Lazy rescaling: the reference max moves only when a score exceeds
+        // it by more than kRescaleSlack (log2 units), so p <= 2^8 and O is
+        // rescaled rarely.  Same softmax; only the rounding differs.
         const bool move = mx > m_run + kRescaleSlack;
         const float m_new = move ? mx : m_run;
         const bool live = m_new != -INFINITY;
         const float alpha = (move && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        float pv[2][4];
         float psum = 0.0f;
-        float pv[4][4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 pv[tt][i] = live ? __builtin_amdgcn_exp2f(z[tt][i] - m_new) : 0.0f;
                 psum += pv[tt][i];
             }
-        }
         psum = wave_xor_sum(psum, 16);
         psum = wave_xor_sum(psum, 32);
         l_run = alpha * l_run + psum;
         m_run = m_new;
-        // any lane of the wave moving its max triggers the (rare) rescale
         if (__any(alpha != 1.0f)) {
 #pragma unroll
             for (int c = 0; c < 32; ++c) o[c] *= alpha;
         }
-        // P as hi + lo bf16 parts (|p - hi - lo| <= 2^-16 |p|): one bf16
-        // rounding of P alone can exceed the output tolerance when V has
-        // large outliers, so PV runs twice per V fragment.
-        bf16x8 ph[2], pl[2];
+        // P as bf16 hi + lo (|p - hi - lo| <= 2^-16 |p|): one bf16 rounding
+        // of P alone can exceed the output tolerance when V has large
+        // outliers.  k-slot j < 4 is token 4gq + j, j >= 4 is token
+        // 16 + 4gq + j - 4 (the same slots as the V^T fragment below).
+        u32x4 h, lo;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            u32x4 h, lo;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float* src = pv[2 * k2 + j];
-                h[2 * j] = pack_bf16_rne(src[0], src[1]);
-                h[2 * j + 1] = pack_bf16_rne(src[2], src[3]);
-                lo[2 * j] = pack_bf16_rne(src[0] - bf16_lo(h[2 * j]), src[1] - bf16_hi(h[2 * j]));
-                lo[2 * j + 1] = pack_bf16_rne(src[2] - bf16_lo(h[2 * j + 1]), src[3] - bf16_hi(h[2 * j + 1]));
-            }
-            ph[k2] = as_bf16x8(h);
-            pl[k2] = as_bf16x8(lo);
+        for (int tt = 0; tt < 2; ++tt) {
+            h[2 * tt] = pack_bf16_rne(pv[tt][0], pv[tt][1]);
+            h[2 * tt + 1] = pack_bf16_rne(pv[tt][2], pv[tt][3]);
+            lo[2 * tt] = pack_bf16_rne(pv[tt][0] - bf16_lo(h[2 * tt]), pv[tt][1] - bf16_hi(h[2 * tt]));
+            lo[2 * tt + 1] = pack_bf16_rne(pv[tt][2] - bf16_lo(h[2 * tt + 1]), pv[tt][3] - bf16_hi(h[2 * tt + 1]));
         }
-        auto vt_frag = [&](int c, int k2) {
-            // tokens 32k2 + 4gq .. +3 and 32k2 + 16 + 4gq .. +3 of element row 16c + c16
-            const uint16_t* rp = &sm.vt[(16 * c + c16) * kVtPitch + 32 * k2 + 4 * gq];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(rp);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(rp + 16);
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8 ph = as_bf16x8(h), pl = as_bf16x8(lo);
+        // V^T fragment of column tile c by transposing reads: within each
+        // 16-lane group, lane s addresses token 4gq + s/4 (+16 for the
+        // second half) and columns 16c + 4(s%4) .. +3; lane i receives the 4
+        // tokens of column 16c + i.
+        const lds_s16x4* vb1 = reinterpret_cast<const lds_s16x4*>(
+            (__attribute__((address_space(3))) const uint16_t*)(ks + (4 * gq + (c16 >> 2)) * kKsPitch + 4 * (c16 & 3)));
+        const lds_s16x4* vb2 = reinterpret_cast<const lds_s16x4*>(
+            (__attribute__((address_space(3))) const uint16_t*)(ks + (16 + 4 * gq + (c16 >> 2)) * kKsPitch + 4 * (c16 & 3)));
+        auto vt_frag = [&](int c) {
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(vb1 + 4 * c));
+            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(vb2 + 4 * c));
+            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
+            return as_bf16x8(u32x4{y1[0], y1[1], y2[0], y2[1]});
         };
-        u32x4 vcur[2], vnxt[2];
-        vcur[0] = vt_frag(0, 0);
-        vcur[1] = vt_frag(0, 1);
+        // two column tiles per step (the hi and lo MFMAs of one accumulator
+        // are separated by the other tile's); fragments one step ahead
+        bf16x8 va = vt_frag(0), vb = vt_frag(1);
 #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            if (c + 1 < 32) {
-                vnxt[0] = vt_frag(c + 1, 0);
-                vnxt[1] = vt_frag(c + 1, 1);
+        for (int c = 0; c < 32; c += 2) {
+            bf16x8 na = va, nb = vb;
+            if (c + 2 < 32) {
+                na = vt_frag(c + 2);
+                nb = vt_frag(c + 3);
             }
-            o[c] = mfma16x16x32(as_bf16x8(vcur[0]), ph[0], o[c]);
-            o[c] = mfma16x16x32(as_bf16x8(vcur[1]), ph[1], o[c]);
-            o[c] = mfma16x16x32(as_bf16x8(vcur[0]), pl[0], o[c]);
-            o[c] = mfma16x16x32(as_bf16x8(vcur[1]), pl[1], o[c]);
+            o[c] = mfma16x16x32(va, ph, o[c]);
+            o[c + 1] = mfma16x16x32(vb, ph, o[c + 1]);
+            o[c] = mfma16x16x32(va, pl, o[c]);
+            o[c + 1] = mfma16x16x32(vb, pl, o[c + 1]);
             __builtin_amdgcn_sched_barrier(0);
-            vcur[0] = vnxt[0];
-            vcur[1] = vnxt[1];
+            va = na;
+            vb = nb;
         }
     };
 
-    if (t_begin < t_end) {
-        if (tid < kTile) compute_offs(t_begin, 0);
+    if (T0 < T1) {
+        if (w == 0) {
+            compute_offs(T0, 0);
+            if (T0 + 1 < T1) compute_offs(T0 + 1, 1);
+            if (T0 + 2 < T1) compute_offs(T0 + 2, 2);
+        }
         __syncthreads();
-        for (int t = t_begin; t < t_end; ++t) {
-            const int buf = (t - t_begin) & 1;
-            load_tile(buf);
-            dequant_tile();
-            if (t + 1 < t_end && tid < kTile) compute_offs(t + 1, buf ^ 1);
-            __syncthreads();
-            if (wave_active) mma_tile(buf);
+        load_raw(0);
+        dequant(0, 0);
+        if (T0 + 1 < T1) load_raw(1);
+        int pos_next = position_of(T0 + 3);
+        __syncthreads();
+        for (int t = T0; t < T1; ++t) {
+            const int i = t - T0;
+            // wavefront 0 resolves tile t+3 in two stages (see above)
+            const int pos_cur = pos_next;
+            int pg_cur = 0;
+            if (w == 0) {
+                pg_cur = page_of(pos_cur);            // issued now, used at the end
+                pos_next = position_of(t + 4);
+            }
+            if (wave_active) compute(i & 1, i & 3);
+            if (t + 1 < T1) dequant((i + 1) & 1, (i + 1) & 3);   // staged during compute(t)
+            if (t + 2 < T1) load_raw((i + 2) & 3);      // lands during compute(t+1)
+            if (w == 0 && lane < kTile && t + 3 < T1) sm.offs[(i + 3) & 3][lane] = offset_of(pos_cur, pg_cur);
             __syncthreads();
         }
     }
 
-    const bool has_head = wave_active && hq < p.H;
     const bool any = l_run > 0.0f;
     const float so = any ? outer / l_run : 0.0f;
     const float lse_v = any ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    const bool has_head = wave_active && hq < p.H;
     if (ns == 1) {
         if (!has_head) return;
         float* dst = p.out + ((int64_t)b * p.H + hq) * kLatent;
@@ -349,8 +356,7 @@ void decode_kernel(DecodeArgs p) {
     }
 
     // Split: write the partial, then the last workgroup of (b, hg) to arrive
-    // merges all ns partials in split order (so the result does not depend
-    // on arrival order) and resets the arrival counter for the next call.
+    // merges all ns partials in split order and resets the arrival counter.
     if (has_head) {
         const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + hq;
         float* dst = p.ws_out + row * kLatent;
@@ -439,18 +445,24 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
 
 template <int NW, bool kRopeFp8, bool kSparse>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.max_splits, (unsigned)a.B, (unsigned)((a.H + 16 * NW - 1) / (16 * NW)));
+    const int hg = 16 * NW;
+    const dim3 grid((unsigned)a.max_splits, (unsigned)a.B, (unsigned)((a.H + hg - 1) / hg));
     hipLaunchKernelGGL((decode_kernel<NW, kRopeFp8, kSparse>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_decode_w(const DecodeArgs& a, hipStream_t stream) {
+    const bool fp8 = a.record_bytes == 368;
+    if (a.indices)
+        return fp8 ? launch_decode_t<NW, true, true>(a, stream) : launch_decode_t<NW, false, true>(a, stream);
+    return fp8 ? launch_decode_t<NW, true, false>(a, stream) : launch_decode_t<NW, false, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    const bool fp8 = a.record_bytes == 368;
-    const bool sparse = a.indices != nullptr;
-    if (sparse) return fp8 ? launch_decode_t<4, true, true>(a, stream) : launch_decode_t<4, false, true>(a, stream);
-    return fp8 ? launch_decode_t<4, true, false>(a, stream) : launch_decode_t<4, false, false>(a, stream);
+    return launch_decode_w<4>(a, stream);
 }
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
