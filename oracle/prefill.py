@@ -68,11 +68,16 @@ def quantize_operands(q, k, v, cu_seqlens, flags, g_q, g_k, g_v, heads=None):
     return qh, kh, vh
 
 
-def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p):
+def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p, p_quantizer=None):
     """Steps 2-4 for one sequence and one head.
 
     qh [L,192], kh [L,192], vh [L,128] (this sequence, float64); ``rows``
     local query indices.  Returns O [len(rows),128], LSE [len(rows)].
+
+    ``p_quantizer(p32, t0)``, if given, replaces step 3's P block QDQ for the
+    tile starting at key t0 (p32: the tile's fp32 probabilities [R, 64]); it
+    lets a test examine the alternatives of P rounding decisions that lie on
+    a rounding boundary.  The default is the NVFP4 block QDQ.
     """
     rows = np.asarray(rows, dtype=np.int64)
     R = rows.size
@@ -96,7 +101,9 @@ def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p):
         alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_safe))
         p = np.where(valid, np.exp(zt - m_safe[:, None]), 0.0)
         l = alpha * l + p.sum(axis=1)
-        if quantize_p:
+        if quantize_p and p_quantizer is not None:
+            p_hat = p_quantizer(p.astype(F32), t0)
+        elif quantize_p:
             p_hat = nvfp4_qdq(p.astype(F32), g_p, axis=-1)
         else:
             p_hat = p

@@ -1,0 +1,257 @@
+"""GPU parity: varlen causal prefill with Q/K/P/V NVFP4 fake quantization and
+NVFP4 output, against the oracle.
+
+Bars:
+* NVFP4 output: at most 0.1% of the compared codes may differ from the
+  oracle's (a differing block scale counts for every code of its block; the
+  two zero codes, +0 and -0, are the same value).  Every difference must be a
+  valid alternative: the GPU accumulates O and l in fp32, the oracle in fp64,
+  so an element (or a block amax) lying within DELTA * (block amax) of an
+  e2m1 (or e4m3) rounding boundary may round either way.  Likewise each P
+  value (fp32 exponential on the GPU) is known to within DELTA relative, so a
+  P block decision within that distance of a boundary may go either way; a
+  row that differs is accepted if some combination of those P decisions
+  reproduces it.  A differing code or scale with no such explanation fails.
+* The dequantized output is within rel-L2 2e-3 of the oracle's dequantized
+  output whenever at least 2^18 elements are compared; below that size one
+  valid near-boundary difference can exceed the bound on its own, and the
+  element-wise validity check above is the binding one.
+* LSE within 1e-3 (natural log).  Scale padding rows are zero.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from mla_attention_nvfp4_amd import ops, workloads
+from oracle import formats as F
+from oracle import prefill as P
+from oracle import swizzle as S
+
+pytestmark = pytest.mark.gpu
+
+CODE_MISMATCH = 1e-3
+REL_L2 = 2e-3
+REL_L2_MIN_ELEMENTS = 1 << 18
+LSE_ABS = 1e-3
+# fp32 accumulation over <= 8192 keys plus fp32 exponentials: a relative error
+# well below 1e-5 of the block maximum; 2^-14 leaves headroom and is still far
+# below the smallest e2m1 step relative to the block maximum (1/12).
+DELTA = 2.0 ** -14
+
+
+def _run_gpu(inp):
+    codes, scales, lse = ops.prefill(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.cu_seqlens.cuda(),
+                                     inp.max_seqlen, inp.softmax_scale, inp.flags, inp.g_q, inp.g_k, inp.g_v,
+                                     inp.g_p, inp.g_out)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), lse.cpu().double().numpy()
+
+
+def _dequant(codes_bhd, sf_rows, g):
+    """codes [R, 64] packed, sf [R, 8] -> float64 [R, 128]."""
+    c = S.unpack_codes(codes_bhd)
+    s = np.repeat(F.e4m3_value(sf_rows), 16, axis=-1)
+    return float(np.float32(g)) * s * F.e2m1_value(c)
+
+
+def _valid(x, gs, gv, g):
+    """Per-element validity of the GPU's (scale code gs [R,8], element value
+    gv [R,128] in e2m1 units) as the quantization of some value within
+    DELTA * amax of the oracle's x [R,128] (fp32 values), block by block."""
+    g32 = np.float32(g)
+    xb = x.reshape(x.shape[0], 8, 16).astype(np.float64)
+    a = np.abs(xb).max(axis=-1)
+    u = np.float32(np.float32(6.0) * g32)
+    s_lo = F.e4m3_encode(((a * (1 - DELTA)) / u).astype(np.float32))
+    s_hi = F.e4m3_encode(((a * (1 + DELTA)) / u).astype(np.float32))
+    scale_ok = (gs >= s_lo) & (gs <= s_hi)
+    d = (F.e4m3_value(gs).astype(np.float32) * g32).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d == 0, np.float32(0.0), np.float32(1.0) / d).astype(np.float32)
+    slack = (DELTA * a)[..., None]
+    lo = F.e2m1_value(F.e2m1_encode(((xb - slack) * inv[..., None]).astype(np.float32)))
+    hi = F.e2m1_value(F.e2m1_encode(((xb + slack) * inv[..., None]).astype(np.float32)))
+    v = gv.reshape(xb.shape)
+    ok = (v >= lo) & (v <= hi) & scale_ok[..., None]
+    return ok.reshape(x.shape)
+
+
+def _block_options(p16, g):
+    """All NVFP4 QDQ results (float64 [16]) of one P block whose fp32 values
+    the GPU knows only to within DELTA relative: the oracle's own result first,
+    then those from the other side of any e4m3 or e2m1 rounding boundary
+    within reach."""
+    g32 = np.float32(g)
+    a = float(np.abs(p16).max())
+    u = np.float32(np.float32(6.0) * g32)
+    t = np.float32(np.float32(a) / u)
+    s0 = int(F.e4m3_encode(t))
+    scales = [s0] + sorted({int(F.e4m3_encode(np.float32(a * f / u))) for f in (1 - DELTA, 1 + DELTA)} - {s0})
+    out = []
+    for s in scales:
+        d = np.float32(np.float32(F.e4m3_value(s)) * g32)
+        inv = np.float32(0.0) if d == 0 else np.float32(np.float32(1.0) / d)
+        x = (p16 * inv).astype(np.float32)
+        c0 = F.e2m1_encode(x)
+        choices = [[int(c)] for c in c0]
+        for f in (1 - DELTA, 1 + DELTA):
+            c1 = F.e2m1_encode((x.astype(np.float64) * f).astype(np.float32))
+            for i in np.nonzero(F.e2m1_value(c1) != F.e2m1_value(c0))[0]:
+                if int(c1[i]) not in choices[i]:
+                    choices[i].append(int(c1[i]))
+        for combo in itertools.product(*choices):
+            out.append(float(g32) * (F.e4m3_value(s) * F.e2m1_value(np.array(combo, dtype=np.uint8))))
+    return out
+
+
+def _row_explained_by_p_ties(inp, n, h, row, gs, gvals):
+    """Whether some combination of near-boundary P rounding decisions makes
+    the oracle's output row (sequence n, local row, head h) quantize to the
+    GPU's scales gs [8] and values gvals [128] (within the O-level check)."""
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    a, b = int(cu[n]), int(cu[n + 1])
+    qh, kh, vh = P.quantize_operands(inp.q[a:b, [h]].float().numpy(), inp.k[a:b, [h]].float().numpy(),
+                                     inp.v[a:b, [h]].float().numpy(), [0, b - a], inp.flags,
+                                     inp.g_q, inp.g_k, inp.g_v)
+    opts = {}
+
+    def record(p32, t0):
+        res = np.empty(p32.shape)
+        for blk in range(p32.shape[1] // 16):
+            o = _block_options(p32[0, 16 * blk:16 * blk + 16], inp.g_p)
+            res[0, 16 * blk:16 * blk + 16] = o[0]
+            if len(o) > 1:
+                opts[(t0, blk)] = o
+        return res
+
+    o_ref, _ = P.attend_rows(qh[:, 0], kh[:, 0], vh[:, 0], [row], inp.softmax_scale, True, inp.g_p, record)
+    keys = sorted(opts)
+    n_comb = int(np.prod([len(opts[k]) for k in keys])) if keys else 1
+    if n_comb > 4096:
+        return False
+    for combo in itertools.product(*[range(len(opts[k])) for k in keys]):
+        pick = dict(zip(keys, combo))
+
+        def quant(p32, t0):
+            res = np.empty(p32.shape)
+            for blk in range(p32.shape[1] // 16):
+                o = _block_options(p32[0, 16 * blk:16 * blk + 16], inp.g_p) if (t0, blk) in pick else None
+                res[0, 16 * blk:16 * blk + 16] = o[pick[(t0, blk)]] if o else \
+                    F.nvfp4_qdq(p32[:, 16 * blk:16 * blk + 16], inp.g_p, axis=-1)[0]
+            return res
+
+        o_row, _ = P.attend_rows(qh[:, 0], kh[:, 0], vh[:, 0], [row], inp.softmax_scale, True, inp.g_p, quant)
+        if _valid(o_row.astype(np.float32), gs[None], gvals[None], inp.g_out).all():
+            return True
+    return False
+
+
+def _compare(inp, gpu, heads, rows_of, what):
+    codes, scales, lse = gpu
+    T, H = inp.T, inp.H
+    sf_gpu = S.unswizzle(scales, T, H * 8)
+    # padding rows of the last 128-row tile are zero
+    tpad = (T + 127) // 128 * 128
+    if tpad > T:
+        mm, cc = np.meshgrid(np.arange(T, tpad), np.arange(H * 8), indexing="ij")
+        assert not scales[S.swizzled_offset(mm, cc, H * 8)].any(), "scale padding rows not zero"
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    hs = np.asarray(heads)
+    q = inp.q[:, hs].float().numpy()
+    k = inp.k[:, hs].float().numpy()
+    v = inp.v[:, hs].float().numpy()
+    O, ref_lse = P.prefill(q, k, v, cu, inp.softmax_scale, inp.flags, inp.g_q, inp.g_k, inp.g_v, inp.g_p,
+                           rows_of=rows_of)
+    rows = ~np.isnan(ref_lse[:, 0])
+    O = np.nan_to_num(O)
+    ref_codes, ref_sf = P.output_nvfp4(O, inp.g_out)          # [T, h', 64], [T, h'*8]
+    ref_sf = ref_sf.reshape(T, len(hs), 8)
+    n_bad = n_all = n_invalid = 0
+    num = den = 0.0
+    mab = lab = 0.0
+    for hi, h in enumerate(hs):
+        gc = codes[rows, h]
+        gs = sf_gpu[rows, 8 * h:8 * h + 8]
+        rc = ref_codes[rows, hi]
+        rs = ref_sf[rows, hi]
+        gvals = F.e2m1_value(S.unpack_codes(gc))
+        rvals = F.e2m1_value(S.unpack_codes(rc))
+        differ = (gvals != rvals) | np.repeat(gs != rs, 16, axis=-1)
+        n_bad += int(differ.sum())
+        n_all += differ.size
+        if differ.any():
+            ok = _valid(O[rows, hi].astype(np.float32), gs, gvals, inp.g_out)
+            bad = differ & ~ok
+            for r in np.unique(np.nonzero(bad)[0]):
+                t = int(np.nonzero(rows)[0][r])
+                n = int(np.searchsorted(cu, t, side="right") - 1)
+                if inp.flags & P.FLAG_P and _row_explained_by_p_ties(inp, n, h, t - int(cu[n]), gs[r], gvals[r]):
+                    print(f"    head {h} row {t}: explained by near-boundary P rounding", flush=True)
+                    bad[r] = False
+            n_invalid += int(bad.sum())
+            for r, c in list(zip(*np.nonzero(bad)))[:5]:
+                print(f"    invalid: head {h} row {np.nonzero(rows)[0][r]} dim {c}: gpu scale {gs[r, c // 16]} "
+                      f"value {gvals[r, c]}, oracle scale {rs[r, c // 16]} value {rvals[r, c]}, "
+                      f"O {O[rows, hi][r, c]:.9g}", flush=True)
+        gd = _dequant(gc, gs, inp.g_out)
+        rd = _dequant(rc, rs, inp.g_out)
+        num += float(((gd - rd) ** 2).sum())
+        den += float((rd ** 2).sum())
+        mab = max(mab, float(np.abs(gd - rd).max()) if gd.size else 0.0)
+        lab = max(lab, float(np.abs(lse[rows, h] - ref_lse[rows, hi]).max()) if rows.any() else 0.0)
+    rel = np.sqrt(num / den) if den > 0 else np.sqrt(num)
+    frac = n_bad / max(n_all, 1)
+    print(f"  {what}: codes differing {n_bad}/{n_all} ({frac:.2e}), not near a rounding boundary {n_invalid}; "
+          f"dequantized rel_l2={rel:.3e} max_abs={mab:.3e}; lse_abs={lab:.3e}", flush=True)
+    assert n_invalid == 0, f"{what}: {n_invalid} differing codes are not near-boundary alternatives"
+    assert frac <= CODE_MISMATCH, f"{what}: {frac:.2e} of codes differ"
+    if n_all >= REL_L2_MIN_ELEMENTS:
+        assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e}"
+    assert lab <= LSE_ABS, f"{what}: lse abs {lab:.3e}"
+
+
+SMALL = [
+    # seed, lens, H, flags
+    (1, [1, 17, 64, 65, 130], 3, 15),
+    (2, [300, 0, 257, 31], 2, 15),
+    (3, [200, 77], 4, 0),
+    (4, [129, 250], 2, 11),   # Q, K, V only
+    (5, [190, 64], 2, 4),     # P only
+    (6, [513], 1, 15),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"prefill{c[0]}-flags{c[3]}" for c in SMALL])
+def test_prefill_small(case):
+    seed, lens, H, flags = case
+    inp = workloads.prefill_inputs(100 + seed, lens, H, flags)
+    print(f"  prefill seed={seed} lens={lens} H={H} flags={flags} T={inp.T}", flush=True)
+    gpu = _run_gpu(inp)
+    _compare(inp, gpu, list(range(H)), None, f"prefill{seed}")
+
+
+def test_prefill_deterministic():
+    inp = workloads.prefill_inputs(120, [300, 200], 2, 15)
+    a = _run_gpu(inp)
+    b = _run_gpu(inp)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_prefill_workload_full_size():
+    """The full prefill workload (8 sequences of 2k-8k tokens, 128 heads, all
+    four quantizers); the oracle checks heads 0, 37, 64, 127 on the first 64,
+    last 64 and 64 random rows of every sequence."""
+    inp = workloads.prefill_workload()
+    print(f"  prefill workload: T={inp.T} max_seqlen={inp.max_seqlen}", flush=True)
+    gpu = _run_gpu(inp)
+    rng = np.random.default_rng(7)
+
+    def rows_of(n, L):
+        r = np.unique(np.concatenate([np.arange(min(64, L)), np.arange(max(0, L - 64), L),
+                                      rng.integers(0, L, 64)]))
+        return r
+
+    _compare(inp, gpu, [0, 37, 64, 127], rows_of, "prefill workload")
+    assert np.all(np.isfinite(gpu[2]))
