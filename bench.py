@@ -129,6 +129,83 @@ class DecodeBench:
         return (t1 - t0) * 1e3 / steps, k_ms
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_B64_H128_L4096_hbm_bytes.md")
+DECODE_SOURCES = ("decode.hip", "device_common.hpp", "launch.hpp")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
+    counter summary, or None when the decode kernel's sources have changed
+    since those counters were taken (the summary records their sha256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line)
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "mla_attention_nvfp4_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if vals.get("decode_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def timed(fn, steps: int, warmup: int) -> float:
+    """Mean ms of fn() over `steps` launches, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def bench_cache_write(inp, steps: int, warmup: int) -> dict:
+    """NVFP4 cache write of every token of the decode workload (T = B*L)."""
+    dev = "cuda"
+    kv, pe = inp.kv_c.to(dev), inp.k_pe.to(dev)
+    slots = inp.slot_mapping.to(dev)
+    cache = torch.zeros((inp.num_pages, inp.page_size, inp.record_bytes), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: ops.cache_write(kv, pe, slots, cache, inp.outer_scale), steps, warmup)
+    T = kv.shape[0]
+    nbytes = T * (576 * 2 + 8 + inp.record_bytes)
+    return {"tokens": T, "kernel_us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": nbytes}
+
+
+def bench_prefill(steps: int, warmup: int) -> dict:
+    """Varlen causal prefill, 8 sequences of 2k-8k tokens, 128 heads, all four
+    operand quantizers, NVFP4 output with swizzled scales and LSE."""
+    inp = workloads.prefill_workload()
+    dev = "cuda"
+    q, k, v, cu = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.cu_seqlens.to(dev)
+    T, H = inp.T, inp.H
+    codes = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    scales = torch.empty(ops.swizzled_scale_bytes(T, H * 8), dtype=torch.uint8, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ops.prefill_workspace_bytes(T, H, inp.flags)), dtype=torch.uint8, device=dev)
+
+    def run():
+        ops.prefill(q, k, v, cu, inp.max_seqlen, inp.softmax_scale, inp.flags, inp.g_q, inp.g_k, inp.g_v,
+                    inp.g_p, inp.g_out, workspace=ws, codes=codes, scales=scales, lse=lse)
+
+    ms = timed(run, steps, warmup)
+    lens = (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1]).tolist()
+    flops = float(sum(H * 320 * L * (L + 1) for L in lens))
+    p_elems = float(sum(H * L * (L + 1) // 2 for L in lens))
+    nbytes = T * H * (192 * 2 * 2 + 128 * 2) + T * H * 64 + scales.numel() + T * H * 4
+    return {"tokens": T, "seq_lens": lens, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
+            "p_elements_per_s": p_elems / (ms * 1e-3), "gbps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(inp, budget_s: float = 12.0):
     """The oracle (unchanged) on whole sequences of the same workload, until
     the time budget is used: queries/s on the host cores."""
@@ -165,8 +242,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-extra", action="store_true", help="skip the 16-head, sparse and prefill lines")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 16-head, sparse, cache-write and prefill measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 3 plain device copies of 256 MiB (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is measured "
@@ -205,7 +285,7 @@ def main():
                                "4 splits + fused merge, plus NVFP4 cache write of 64 new tokens",
                    "global_batch": B, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "kernel": "decode_kernel", "kernel_us": k_ms * 1e3,
                      "flops_per_launch": flops, "bytes_per_launch": nbytes},
         "hbm": {"achieved_gbps": gbps, "peak_gbps": PEAK_HBM_GBPS, "frac": gbps / PEAK_HBM_GBPS},
@@ -237,7 +317,23 @@ def main():
                                   "queries_per_s": inp3.B / (k3 * 1e-3), "valid_indices": nvalid}
         del b3, inp3
         torch.cuda.empty_cache()
+        log("cache write of the decode workload's 262,144 tokens")
+        paths["cache_write"] = bench_cache_write(inp, max(10, args.steps // 2), 3)
+        torch.cuda.empty_cache()
+        log("prefill (8 sequences of 2k-8k tokens, 128 heads, NVFP4 output)")
+        paths["prefill"] = bench_prefill(max(3, args.steps // 10), 1)
+        torch.cuda.empty_cache()
         result["paths"] = paths
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
 
     if not args.no_cpu:
         log("oracle CPU baseline")

@@ -211,9 +211,10 @@ def lse_merge(partial_out, partial_lse, splits_per_seq=None, out=None, lse=None)
 
 
 def prefill(q, k, v, cu_seqlens, max_seqlen, softmax_scale, flags, g_q, g_k, g_v, g_p, out_global_scale,
-            with_lse=True, workspace=None):
+            with_lse=True, workspace=None, codes=None, scales=None, lse=None):
     """Varlen causal prefill with NVFP4 output.  Returns (codes uint8 [T,H,64],
-    swizzled scales uint8, lse fp32 [T,H] or None)."""
+    swizzled scales uint8, lse fp32 [T,H] or None); the three outputs may be
+    passed in (then they are filled and returned)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, n)
     _need(cu_seqlens, torch.int32, "cu_seqlens")
@@ -222,9 +223,20 @@ def prefill(q, k, v, cu_seqlens, max_seqlen, softmax_scale, flags, g_q, g_k, g_v
             or q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1:
         raise ValueError("q, k [T,H,192] and v [T,H,128] with unit inner stride")
     dev = q.device
-    codes = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
-    scales = torch.empty(max(1, swizzled_scale_bytes(T, H * 8)), dtype=torch.uint8, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if with_lse else None
+    if codes is None:
+        codes = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(max(1, swizzled_scale_bytes(T, H * 8)), dtype=torch.uint8, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if codes.shape != (T, H, 64) or not codes.is_contiguous() or scales.numel() < swizzled_scale_bytes(T, H * 8):
+        raise ValueError("codes must be contiguous [T,H,64] and scales hold the swizzled scale buffer")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        if lse.shape != (T, H) or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous [T,H]")
     need = prefill_workspace_bytes(T, H, flags)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
