@@ -84,7 +84,7 @@ class DecodeBench:
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         need = ops.decode_workspace_bytes(B, H, inp.max_splits)
-        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
         # the step's new tokens overwrite the last position of every sequence
         g = torch.Generator().manual_seed(1234)
         self.new_kv = torch.randn((B, 576), generator=g).to(torch.bfloat16).to(dev)

@@ -89,12 +89,10 @@ int mla_nvfp4_record_bytes(int rope_fp8);
 int mla_decode_num_splits(int seq_len, int max_splits);
 
 /* Bytes of decode workspace for B sequences, H heads, max_splits chunks:
- * partial outputs fp32 [B][max_splits][H][512], partial LSE fp32
- * [B][max_splits][H], then int32 arrival counters [B][ceil(H/16)], each
- * region 256-byte aligned.  0 when max_splits <= 1.  The workspace must be
- * zero-filled before its first use; every completed call leaves the counters
- * at zero again, so one workspace serves any number of stream-ordered calls
- * (calls that may run concurrently need separate workspaces). */
+ * partial outputs fp32 [B][max_splits][H][512], then partial LSE fp32
+ * [B][max_splits][H], each region 256-byte aligned.  0 when
+ * max_splits <= 1.  No initial contents are needed; calls that may run
+ * concurrently need separate workspaces. */
 size_t mla_decode_workspace_bytes(int B, int H, int max_splits);
 
 /* Bytes of a 128x4-swizzled e4m3 scale buffer for `rows` rows of
@@ -151,14 +149,15 @@ int mla_nvfp4_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride,
  *  max_splits      >= 1; sequence b is split into
  *                  mla_decode_num_splits(L, max_splits) chunks whose
  *                  (out, lse) partials are merged as mla_lse_merge does
- *  workspace       >= mla_decode_workspace_bytes(B, H, max_splits) bytes,
- *                  zero-filled before first use (may be NULL when
- *                  max_splits == 1)
+ *  workspace       >= mla_decode_workspace_bytes(B, H, max_splits) bytes
+ *                  (may be NULL when max_splits == 1)
  *  out, lse        fp32 [B, H, 512] and [B, H]
  *
  * Kernel-side checks: a page id outside [0, num_pages) masks that token.
- * One launch on `stream`; within it the last workgroup to finish a
- * sequence's chunks merges them in chunk order (bitwise deterministic). */
+ * Enqueued on `stream`: the decode kernel, which writes single-chunk
+ * sequences directly and the partials of split ones to the workspace, then
+ * (max_splits > 1) a merge kernel combining each split sequence's partials
+ * in chunk order (bitwise deterministic). */
 int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
                      int64_t q_stride_b, int64_t q_stride_h,
                      const uint8_t* cache, int64_t num_pages, int record_bytes,

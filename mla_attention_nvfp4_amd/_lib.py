@@ -151,8 +151,7 @@ def _workspace(B, H, max_splits, like, workspace):
     if need == 0:
         return None
     if workspace is None:
-        # zero-filled on first use; the kernels leave it reusable
-        workspace = torch.zeros(need, dtype=torch.uint8, device=like.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=like.device)
     return workspace
 
 

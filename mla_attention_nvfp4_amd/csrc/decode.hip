@@ -54,7 +54,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 struct DecodeSmem {
     uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
     int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
-    int last;                             // this workgroup merges the splits
 };
 
 
@@ -355,56 +354,58 @@ void decode_kernel(DecodeArgs p) {
         return;
     }
 
-    // Split: write the partial, then the last workgroup of (b, hg) to arrive
-    // merges all ns partials in split order and resets the arrival counter.
-    if (has_head) {
-        const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + hq;
-        float* dst = p.ws_out + row * kLatent;
-        if (gq == 0) p.ws_lse[row] = lse_v;
+    // Split: write the partial; split_merge_kernel combines them.
+    if (!has_head) return;
+    const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + hq;
+    float* dst = p.ws_out + row * kLatent;
+    if (gq == 0) p.ws_lse[row] = lse_v;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+    for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+}
+
+// Merge of the split partials of a decode launch, one wavefront per (b, h)
+// (same rule as lse_merge_kernel, splits in order); sequences with a single
+// split were written directly by the decode kernel.
+template <bool kSparse>
+__global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wid >= p.B * p.H) return;
+    const int b = wid / p.H, h = wid % p.H;
+    int L = p.seq_lens[b];
+    const int Lmax = p.max_pages * p.page_size;
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int ns = decode_num_splits(kSparse ? p.topk : L, p.max_splits);
+    if (ns <= 1) return;
+    const int64_t row0 = (int64_t)b * p.max_splits * p.H + h;   // split s at row0 + s*H
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_lse[row0 + (int64_t)s * p.H]);
+    float* dst = p.out + ((int64_t)b * p.H + h) * kLatent + 8 * lane;
+    if (M == -INFINITY) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (lane == 0) p.lse[(int64_t)b * p.H + h] = -INFINITY;
+        return;
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        int* cnt = p.ws_count + (int64_t)b * p.count_stride + hg;
-        const int old = atomicAdd(cnt, 1);
-        sm.last = (old == ns - 1);
-        if (old == ns - 1) atomicExch(cnt, 0);
+    float wsum = 0.0f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const int64_t row = row0 + (int64_t)s * p.H;
+        const float l = p.ws_lse[row];
+        const float* src = p.ws_out + row * kLatent + 8 * lane;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        if (l == -INFINITY) continue;
+        const float wgt = expf(l - M);
+        wsum += wgt;
+        a0 += wgt * x0;
+        a1 += wgt * x1;
     }
-    __syncthreads();
-    if (!sm.last || !wave_active) return;
-    __threadfence();
-    for (int j = 0; j < 16; ++j) {
-        const int h = h_base + j;
-        if (h >= p.H) break;
-        const int64_t row0 = (int64_t)b * p.max_splits * p.H + h;   // split s2 at row0 + s2*H
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, p.ws_lse[row0 + (int64_t)s2 * p.H]);
-        float* dst = p.out + ((int64_t)b * p.H + h) * kLatent + 8 * lane;
-        if (M == -INFINITY) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (lane == 0) p.lse[(int64_t)b * p.H + h] = -INFINITY;
-            continue;
-        }
-        float wsum = 0.0f;
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < ns; ++s2) {
-            const int64_t row = row0 + (int64_t)s2 * p.H;
-            const float l = p.ws_lse[row];
-            if (l == -INFINITY) continue;
-            const float wgt = expf(l - M);
-            wsum += wgt;
-            const float* src = p.ws_out + row * kLatent + 8 * lane;
-            a0 += wgt * *reinterpret_cast<const f32x4*>(src);
-            a1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
-        }
-        const float inv = 1.0f / wsum;
-        *reinterpret_cast<f32x4*>(dst) = a0 * inv;
-        *reinterpret_cast<f32x4*>(dst + 4) = a1 * inv;
-        if (lane == 0) p.lse[(int64_t)b * p.H + h] = M + logf(wsum);
-    }
+    const float inv = 1.0f / wsum;
+    *reinterpret_cast<f32x4*>(dst) = a0 * inv;
+    *reinterpret_cast<f32x4*>(dst + 4) = a1 * inv;
+    if (lane == 0) p.lse[(int64_t)b * p.H + h] = M + logf(wsum);
 }
 
 // One wavefront merges one (b, h).
@@ -448,6 +449,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int hg = 16 * NW;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.B, (unsigned)((a.H + hg - 1) / hg));
     hipLaunchKernelGGL((decode_kernel<NW, kRopeFp8, kSparse>), grid, dim3(NW * 64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_splits <= 1) return e;
+    const int64_t waves = (int64_t)a.B * a.H;
+    hipLaunchKernelGGL((split_merge_kernel<kSparse>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -31,8 +31,6 @@ struct DecodeArgs {
     int max_splits;
     float* ws_out;            // [B][max_splits][H][512] (null if max_splits == 1)
     float* ws_lse;            // [B][max_splits][H]
-    int* ws_count;            // [B][count_stride] arrival counters, zero between calls
-    int count_stride;         // ceil(H / 16)
     float* out;               // [B][H][512]
     float* lse;               // [B][H]
 };

@@ -37,7 +37,7 @@ def test_constants_and_policy():
             k = L.decode_num_splits(n, s)
             tiles = (n + 63) // 64
             assert 1 <= k <= s and k <= tiles
-    assert L.decode_workspace_bytes(64, 128, 4) == 64 * 4 * 128 * 512 * 4 + 64 * 4 * 128 * 4 + 64 * 8 * 4
+    assert L.decode_workspace_bytes(64, 128, 4) == 64 * 4 * 128 * 512 * 4 + 64 * 4 * 128 * 4
     assert L.decode_workspace_bytes(64, 128, 1) == 0
     assert L.swizzled_scale_bytes(1, 1) == 128 * 4
     assert L.swizzled_scale_bytes(129, 1024) == 256 * 1024
