@@ -8,7 +8,7 @@
 // the per-layer outer scale on read; review 2: Q is staged as bf16 with no
 // Q quantization.
 //
-// Work item: workgroup (split s, sequence b, head group hg) of NW
+// Work item: workgroup (split s, sequence b, head group hg) of NW (= 8)
 // wavefronts, each owning 16 query heads.  The split's tokens are walked in
 // tiles of 32, software-pipelined:
 //   offsets   record byte offsets (page-table walk) of tile t+3 into a ring
@@ -97,8 +97,9 @@ void decode_kernel(DecodeArgs p) {
     }
 
     const uint8_t* __restrict__ cache = p.cache;
-    const float scale_log2 = p.softmax_scale * kLog2e;
     const float outer = p.outer_scale;
+    const float inv_outer = 1.0f / outer;
+    const float score_scale = p.softmax_scale * kLog2e * outer;
 
     // ---- offsets.  Loads are issued by every lane of wavefront 0 from
     // clamped (always valid) addresses and masked afterwards, so the
@@ -194,38 +195,34 @@ void decode_kernel(DecodeArgs p) {
 
     auto compute = [&](int kbuf, int slot) {
         const uint16_t* ks = sm.ks[kbuf];
-        // S^T accumulators: latent k-steps alternate between two sets so
-        // consecutive MFMAs are independent; the latent part is multiplied
-        // by the outer scale before the RoPE k-steps are added.
-        f32x4 sa[2], sb[2];
-        sa[0] = sa[1] = sb[0] = sb[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // S^T accumulators, one per 16-token half of the tile (consecutive
+        // MFMAs alternate between them): the RoPE k-steps go first, the
+        // accumulators are then divided by the outer scale, and the latent
+        // k-steps follow, so that outer * S restores the scale on the latent
+        // part only.
+        f32x4 sa[2];
+        sa[0] = sa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto ks_frag = [&](int kk, int tt) {
             return *reinterpret_cast<const u32x4*>(&ks[(16 * tt + c16) * kKsPitch + 32 * kk + 8 * gq]);
         };
-        // fragments two k-steps ahead of their MFMAs
-        u32x4 f0[3], f1[3];
-        f0[0] = ks_frag(0, 0);
-        f1[0] = ks_frag(0, 1);
-        f0[1] = ks_frag(1, 0);
-        f1[1] = ks_frag(1, 1);
+        auto order = [](int i) { return i < 2 ? 16 + i : i - 2; };
+        // fragments one k-step ahead of their MFMAs
+        u32x4 f0[2], f1[2];
+        f0[0] = ks_frag(order(0), 0);
+        f1[0] = ks_frag(order(0), 1);
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-            if (kk + 2 < 18) {
-                f0[(kk + 2) % 3] = ks_frag(kk + 2, 0);
-                f1[(kk + 2) % 3] = ks_frag(kk + 2, 1);
+        for (int i = 0; i < 18; ++i) {
+            if (i + 1 < 18) {
+                f0[(i + 1) & 1] = ks_frag(order(i + 1), 0);
+                f1[(i + 1) & 1] = ks_frag(order(i + 1), 1);
             }
-            const u32x4 a0 = f0[kk % 3], a1 = f1[kk % 3];
-            if (kk < 16 && (kk & 1)) {
-                sb[0] = mfma16x16x32(as_bf16x8(a0), qf[kk], sb[0]);
-                sb[1] = mfma16x16x32(as_bf16x8(a1), qf[kk], sb[1]);
-            } else {
-                sa[0] = mfma16x16x32(as_bf16x8(a0), qf[kk], sa[0]);
-                sa[1] = mfma16x16x32(as_bf16x8(a1), qf[kk], sa[1]);
+            if (i == 2) {
+                sa[0] *= inv_outer;
+                sa[1] *= inv_outer;
             }
-            if (kk == 15) {
-                sa[0] = (sa[0] + sb[0]) * outer;
-                sa[1] = (sa[1] + sb[1]) * outer;
-            }
+            const int kk = order(i);
+            sa[0] = mfma16x16x32(as_bf16x8(f0[i & 1]), qf[kk], sa[0]);
+            sa[1] = mfma16x16x32(as_bf16x8(f1[i & 1]), qf[kk], sa[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
@@ -236,7 +233,7 @@ void decode_kernel(DecodeArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool valid = sm.offs[slot][16 * tt + 4 * gq + i] >= 0;
-                z[tt][i] = valid ? scale_log2 * sa[tt][i] : -INFINITY;
+                z[tt][i] = valid ? score_scale * sa[tt][i] : -INFINITY;
                 mx = fmaxf(mx, z[tt][i]);
             }
         mx = wave_xor_max(mx, 16);
@@ -293,22 +290,15 @@ void decode_kernel(DecodeArgs p) {
             return as_bf16x8(u32x4{y1[0], y1[1], y2[0], y2[1]});
         };
         // two column tiles per step (the hi and lo MFMAs of one accumulator
-        // are separated by the other tile's); fragments one step ahead
-        bf16x8 va = vt_frag(0), vb = vt_frag(1);
+        // are separated by the other tile's)
 #pragma unroll
         for (int c = 0; c < 32; c += 2) {
-            bf16x8 na = va, nb = vb;
-            if (c + 2 < 32) {
-                na = vt_frag(c + 2);
-                nb = vt_frag(c + 3);
-            }
+            const bf16x8 va = vt_frag(c), vb = vt_frag(c + 1);
             o[c] = mfma16x16x32(va, ph, o[c]);
             o[c + 1] = mfma16x16x32(vb, ph, o[c + 1]);
             o[c] = mfma16x16x32(va, pl, o[c]);
             o[c + 1] = mfma16x16x32(vb, pl, o[c + 1]);
             __builtin_amdgcn_sched_barrier(0);
-            va = na;
-            vb = nb;
         }
     };
 
@@ -467,7 +457,7 @@ hipError_t launch_decode_w(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    return launch_decode_w<4>(a, stream);
+    return launch_decode_w<8>(a, stream);
 }
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
