@@ -51,10 +51,24 @@ constexpr float kRescaleSlack = 8.0f;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Q k-steps kept in LDS (B-operand layout, 16 B per lane) instead of
+// registers: the RoPE part and the first kQLdsLatent latent k-steps.
+constexpr int kQLdsLatent = 6;
+constexpr int kQLds = kQLdsLatent + 2;
+
+template <int NW>
 struct DecodeSmem {
     uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
+    u32x4 qs[NW][kQLds][64];              // NW x 6 KB
     int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
 };
+
+// LDS-only workgroup barrier: this wavefront's LDS operations are complete
+// before it arrives; outstanding global loads stay in flight.  (The asm's
+// memory clobber keeps the compiler from moving memory accesses across.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 
 template <int NW, bool kRopeFp8, bool kSparse>
@@ -62,7 +76,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 void decode_kernel(DecodeArgs p) {
     constexpr int kRec = kRopeFp8 ? 368 : 432;
     constexpr int kRpw = kTile / NW;                         // records per wavefront
-    __shared__ DecodeSmem sm;
+    __shared__ DecodeSmem<NW> sm;
 
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -82,18 +96,24 @@ void decode_kernel(DecodeArgs p) {
     const bool wave_active = h_base < p.H;
     const int hq = h_base + c16;
 
-    // Q as the B operand of S^T = K Q^T: k-step kk covers d = 32kk..32kk+31.
-    bf16x8 qf[18];
+    // Q as the B operand of S^T = K Q^T: k-step kk covers d = 32kk..32kk+31
+    // (kk 16, 17: RoPE).  Latent k-steps kQLdsLatent..15 stay in registers
+    // (qf[kk - kQLdsLatent]); the others go to this wavefront's LDS slots
+    // (slot kk for kk < kQLdsLatent, kQLdsLatent + kk - 16 for RoPE).
+    bf16x8 qf[16 - kQLdsLatent];
     {
         const bool ok = hq < p.H;
         const u32x4 zero = {0u, 0u, 0u, 0u};
         const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(ok ? hq : 0) * p.q_stride_h + 8 * gq;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-            qf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero);
+        for (int kk = 0; kk < 16; ++kk) {
+            const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero;
+            if (kk < kQLdsLatent) sm.qs[w][kk][lane] = v;
+            else qf[kk - kQLdsLatent] = as_bf16x8(v);
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            qf[16 + kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(p.q_rope + qoff + 32 * kk) : zero);
+            sm.qs[w][kQLdsLatent + kk][lane] = ok ? *reinterpret_cast<const u32x4*>(p.q_rope + qoff + 32 * kk) : zero;
     }
 
     const uint8_t* __restrict__ cache = p.cache;
@@ -206,23 +226,28 @@ void decode_kernel(DecodeArgs p) {
             return *reinterpret_cast<const u32x4*>(&ks[(16 * tt + c16) * kKsPitch + 32 * kk + 8 * gq]);
         };
         auto order = [](int i) { return i < 2 ? 16 + i : i - 2; };
-        // fragments one k-step ahead of their MFMAs
-        u32x4 f0[2], f1[2];
+        auto q_lds = [](int kk) { return kk < kQLdsLatent || kk >= 16; };
+        auto q_slot = [](int kk) { return kk < kQLdsLatent ? kk : kQLdsLatent + kk - 16; };
+        // fragments (and LDS-held Q) one k-step ahead of their MFMAs
+        u32x4 f0[2], f1[2], qb[2];
         f0[0] = ks_frag(order(0), 0);
         f1[0] = ks_frag(order(0), 1);
+        qb[0] = sm.qs[w][q_slot(order(0))][lane];
 #pragma unroll
         for (int i = 0; i < 18; ++i) {
             if (i + 1 < 18) {
                 f0[(i + 1) & 1] = ks_frag(order(i + 1), 0);
                 f1[(i + 1) & 1] = ks_frag(order(i + 1), 1);
+                if (q_lds(order(i + 1))) qb[(i + 1) & 1] = sm.qs[w][q_slot(order(i + 1))][lane];
             }
             if (i == 2) {
                 sa[0] *= inv_outer;
                 sa[1] *= inv_outer;
             }
             const int kk = order(i);
-            sa[0] = mfma16x16x32(as_bf16x8(f0[i & 1]), qf[kk], sa[0]);
-            sa[1] = mfma16x16x32(as_bf16x8(f1[i & 1]), qf[kk], sa[1]);
+            const bf16x8 qv = q_lds(kk) ? as_bf16x8(qb[i & 1]) : qf[kk - kQLdsLatent];
+            sa[0] = mfma16x16x32(as_bf16x8(f0[i & 1]), qv, sa[0]);
+            sa[1] = mfma16x16x32(as_bf16x8(f1[i & 1]), qv, sa[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
@@ -323,11 +348,21 @@ void decode_kernel(DecodeArgs p) {
                 pg_cur = page_of(pos_cur);            // issued now, used at the end
                 pos_next = position_of(t + 4);
             }
+            // The two halves of the workgroup run the phases in opposite
+            // order, so that each SIMD holds one wavefront in its MFMA phase
+            // while the other dequantizes.
+            const bool late = w >= NW / 2;
+            if (late && t + 1 < T1) {
+                dequant((i + 1) & 1, (i + 1) & 3);
+                if (t + 2 < T1) load_raw((i + 2) & 3);   // lands during tile t+1
+            }
             if (wave_active) compute(i & 1, i & 3);
-            if (t + 1 < T1) dequant((i + 1) & 1, (i + 1) & 3);   // staged during compute(t)
-            if (t + 2 < T1) load_raw((i + 2) & 3);      // lands during compute(t+1)
+            if (!late && t + 1 < T1) {
+                dequant((i + 1) & 1, (i + 1) & 3);
+                if (t + 2 < T1) load_raw((i + 2) & 3);
+            }
             if (w == 0 && lane < kTile && t + 3 < T1) sm.offs[(i + 3) & 3][lane] = offset_of(pos_cur, pg_cur);
-            __syncthreads();
+            lds_barrier();
         }
     }
 
