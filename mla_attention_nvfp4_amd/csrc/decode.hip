@@ -53,7 +53,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Q k-steps kept in LDS (B-operand layout, 16 B per lane) instead of
 // registers: the RoPE part and the first kQLdsLatent latent k-steps.
-constexpr int kQLdsLatent = 6;
+constexpr int kQLdsLatent = 8;
 constexpr int kQLds = kQLdsLatent + 2;
 
 template <int NW>
@@ -61,7 +61,27 @@ struct DecodeSmem {
     uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
     u32x4 qs[NW][kQLds][64];              // NW x 6 KB
     int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
+    uint32_t valid[kRing];                // bit i: token i of the tile is unmasked
 };
+
+// op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]) by the gfx950 row-swap
+// permutes (each returns {x[l], x[l ^ 16 or 32]} in some order).
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
 
 // LDS-only workgroup barrier: this wavefront's LDS operations are complete
 // before it arrives; outstanding global loads stay in flight.  (The asm's
@@ -138,10 +158,14 @@ void decode_kernel(DecodeArgs p) {
         return (pos >= 0 && pg >= 0 && pg < p.num_pages)
                    ? ((int64_t)pg * p.page_size + pos % p.page_size) * kRec : int64_t(-1);
     };
+    auto store_offs = [&](int slot, int64_t off) {
+        const uint64_t vm = __ballot(lane < kTile && off >= 0);
+        if (lane < kTile) sm.offs[slot][lane] = off;
+        if (lane == 0) sm.valid[slot] = (uint32_t)vm;
+    };
     auto compute_offs = [&](int t, int slot) {
         const int pos = position_of(t);
-        const int64_t off = offset_of(pos, page_of(pos));
-        if (lane < kTile) sm.offs[slot][lane] = off;
+        store_offs(slot, offset_of(pos, page_of(pos)));
     };
 
     // ---- staging: this wavefront's records kRpw*w .. +kRpw-1 of a tile in
@@ -176,10 +200,11 @@ void decode_kernel(DecodeArgs p) {
     // lane = 16-byte column chunk (8 latent elements)
     auto dequant = [&](int kbuf, int slot) {
         uint16_t* ks = sm.ks[kbuf];
+        const uint32_t vmask = sm.valid[slot];
 #pragma unroll
         for (int r = 0; r < kRpw; ++r) {
             const int tok = kRpw * w + r;
-            const bool valid = sm.offs[slot][tok] >= 0;
+            const bool valid = (vmask >> tok) & 1u;
             const uint32_t c = valid ? rc[r] : 0u;
             const float sc = e4m3_decode(valid ? rs[r] : 0u);
             const f32x2 v0 = e2m1_pair<0>(c), v1 = e2m1_pair<1>(c);
@@ -191,7 +216,7 @@ void decode_kernel(DecodeArgs p) {
         // RoPE: kRpw tokens x 8 units of 8 elements
         if (lane < 8 * kRpw) {
             const int tok = kRpw * w + (lane >> 3), u = lane & 7;
-            const bool valid = sm.offs[slot][tok] >= 0;
+            const bool valid = (vmask >> tok) & 1u;
             u32x4 wv;
             if (kRopeFp8) {
 #pragma unroll
@@ -253,16 +278,16 @@ void decode_kernel(DecodeArgs p) {
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
         float z[2][4];
         float mx = -INFINITY;
+        const uint32_t vmask = sm.valid[slot];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = sm.offs[slot][16 * tt + 4 * gq + i] >= 0;
+                const bool valid = (vmask >> (16 * tt + 4 * gq + i)) & 1u;
                 z[tt][i] = valid ? score_scale * sa[tt][i] : -INFINITY;
                 mx = fmaxf(mx, z[tt][i]);
             }
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
+        mx = xor32_max(xor16_max(mx));
         // Lazy rescaling: the reference max moves only when a score exceeds
         // it by more than kRescaleSlack (log2 units), so p <= 2^8 and O is
         // rescaled rarely.  Same softmax; only the rounding differs.
@@ -279,8 +304,7 @@ void decode_kernel(DecodeArgs p) {
                 pv[tt][i] = live ? __builtin_amdgcn_exp2f(z[tt][i] - m_new) : 0.0f;
                 psum += pv[tt][i];
             }
-        psum = wave_xor_sum(psum, 16);
-        psum = wave_xor_sum(psum, 32);
+        psum = xor32_sum(xor16_sum(psum));
         l_run = alpha * l_run + psum;
         m_run = m_new;
         if (__any(alpha != 1.0f)) {
@@ -361,7 +385,7 @@ void decode_kernel(DecodeArgs p) {
                 dequant((i + 1) & 1, (i + 1) & 3);
                 if (t + 2 < T1) load_raw((i + 2) & 3);
             }
-            if (w == 0 && lane < kTile && t + 3 < T1) sm.offs[(i + 3) & 3][lane] = offset_of(pos_cur, pg_cur);
+            if (w == 0 && t + 3 < T1) store_offs((i + 3) & 3, offset_of(pos_cur, pg_cur));
             lds_barrier();
         }
     }
