@@ -29,10 +29,11 @@ CFLAGS = [
 ]
 
 
-# Per-source extra flags.  decode.hip: MFMA accumulators in VGPRs, so the
+# Per-source extra flags.  decode kernels: MFMA accumulators in VGPRs, so the
 # (rare) softmax rescale of the output accumulators needs no AGPR round trip
 # and the loop-carried accumulators are not copied between register files.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

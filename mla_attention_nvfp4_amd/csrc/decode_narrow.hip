@@ -1,0 +1,395 @@
+// Paged absorbed split-K MLA decode over the NVFP4 latent cache for narrow
+// head groups (H <= 16), where the path is bound by HBM: every wavefront
+// streams its own tokens, with no workgroup barrier in the token loop.
+//
+// [MO-MLA], commit 1: split-K absorbed MQA decode over the paged latent with
+// grouped query heads and a natural-log LSE for merging; commit 3: V is the
+// stored latent itself.  [B12X], walkthrough and sequence diagram: the
+// decode kernel stages NVFP4 data, dequantizes it and accumulates, restoring
+// the per-layer outer scale on read; review 2: Q is not quantized.
+//
+// Work item: workgroup (split s, sequence b) of 4 wavefronts; wavefront w
+// takes the split's 16-token tiles w, w+4, ...  Per tile, software-
+// pipelined: page-table walk three tiles ahead, record loads two tiles ahead
+// into registers, then
+//   S^T = K Q^T (16 tokens x 16 heads).  Lane l covers token l%16 and the
+//     latent dims 128(l/16) .. +127 (k-step kk: dims 128(l/16) + 8kk .. +7;
+//     the k-slot order is a permutation shared by both operands), so each
+//     lane dequantizes the 64 code bytes and 8 scales of its own token
+//     straight into the MFMA operand: e2m1 x e4m3 is exact in fp16 (at most
+//     6 significant bits, magnitudes in [2^-10, 2688]), by the gfx950 FP4
+//     conversion and one packed fp16 multiply per two elements.  Q's latent
+//     part is held in fp16 after an exact per-head power-of-two scaling
+//     (bf16 has 8 significant bits); the RoPE k-steps stay in bf16, since
+//     arbitrary bf16 RoPE values need not fit fp16's range.
+//   online softmax in base 2 with lazy rescaling; P as fp16 hi + lo
+//     (|p - hi - lo| <= 2^-22 |p|);
+//   O^T = V^T P^T with v_mfma_f32_16x16x16_f16: the dequantized latent
+//     goes to this wavefront's own LDS tile (token-major) and V^T is read
+//     back by ds_read_b64_tr_b16.
+// The four wavefronts then merge their (O, m, l) in LDS; single-split
+// sequences are written out, split ones go to the workspace for
+// split_merge_kernel.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kNW = 4;            // wavefronts per workgroup
+constexpr int kNT = 16;           // tokens per wavefront tile
+constexpr int kVP = 528;          // fp16 per V tile row (1056 B: conflict-free writes and transposed reads)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;
+
+struct NarrowSmem {
+    _Float16 vt[kNW][kNT * kVP];  // 4 x 16,896 B; reused for the output merge
+    float m[kNW][16], l[kNW][16];
+};
+
+__device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// D = A (16x16) * B (16x16) + C; lane l supplies row / column l % 16 with
+// k-slots 4*(l/16) .. +3 and receives D[4*(l/16) + i][l % 16].
+__device__ __forceinline__ f32x4 mfma_k16_f16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+
+// The record bytes one lane needs for its token: 64 code bytes, 8 scale
+// bytes, and its RoPE share (32 B bf16 or 16 B e4m3).
+struct Staged {
+    u32x4 c[4];
+    u32x2 sc;
+    u32x4 r[2];
+};
+
+template <bool kRopeFp8, bool kSparse>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_narrow_kernel(DecodeArgs p) {
+    constexpr int kRec = kRopeFp8 ? 368 : 432;
+    __shared__ NarrowSmem sm;
+
+    const int s = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c16 = lane & 15, gq = lane >> 4;
+
+    int L = p.seq_lens[b];
+    const int Lmax = p.max_pages * p.page_size;
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int n_items = kSparse ? p.topk : L;
+    const int ns = decode_num_splits(n_items, p.max_splits);
+    if (s >= ns) return;
+    const int ct = decode_chunk_tiles(n_items, p.max_splits);   // in 64-item units
+    const int i0 = 64 * ct * s;
+    const int i1 = min(n_items, i0 + 64 * ct);
+    const int ntiles = (i1 - i0 + kNT - 1) / kNT;
+    const int nmine = ntiles > w ? (ntiles - w + kNW - 1) / kNW : 0;   // tiles w, w+4, ...
+
+    const bool hok = c16 < p.H;
+
+    // ---- Q.  Latent (B operand of the fp16 k-steps): lane holds head c16,
+    // dims 128gq + 8kk .. +7 for kk = 0..15, scaled by 2^(14 - E) where 2^E
+    // <= max |q_nope| of the head < 2^(E+1) (exact; the largest value lands
+    // in [2^14, 2^15)).  RoPE (bf16 k-steps kr = 0, 1): dims 16gq + 8kr .. +7.
+    f16x8 qf[16];
+    bf16x8 qr[2];
+    float q_unscale;   // 2^(E - 14)
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const uint16_t* qn = p.q_nope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 128 * gq;
+        const uint16_t* qp = p.q_rope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 16 * gq;
+        u32x4 raw[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            raw[kk] = hok ? *reinterpret_cast<const u32x4*>(qn + 8 * kk) : zero;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(raw[kk][j])), __builtin_fabsf(bf16_hi(raw[kk][j]))));
+        }
+        amax = xor32_max(xor16_max(amax));
+        int E = amax > 0.0f ? (int)((f2u(amax) >> 23) & 0xffu) - 127 : 0;
+        E = E < -100 ? -100 : E;
+        const int sh = 14 - E;
+        q_unscale = __builtin_ldexpf(1.0f, E - 14);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            f16x8 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(raw[kk][j]), sh);
+                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(raw[kk][j]), sh);
+            }
+            qf[kk] = v;
+        }
+#pragma unroll
+        for (int kr = 0; kr < 2; ++kr) qr[kr] = as_bf16x8(hok ? *reinterpret_cast<const u32x4*>(qp + 8 * kr) : zero);
+    }
+
+    const uint8_t* __restrict__ cache = p.cache;
+    const float outer = p.outer_scale;
+    const float sc_rope = p.softmax_scale * kLog2e;
+    const float sc_lat = sc_rope * outer * q_unscale;
+
+    // ---- token addressing: tile j of this wavefront covers items
+    // i0 + kNT*(w + kNW*j) .. +15; lane l handles item + c16.
+    auto item_of = [&](int j) { return i0 + kNT * (w + kNW * j) + c16; };
+    auto position_of = [&](int j) -> int {
+        const int item = item_of(j);
+        const int ic = min(item, max(n_items - 1, 0));
+        const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
+        return (j < nmine && item < i1 && pos >= 0 && pos < L) ? pos : -1;
+    };
+    auto page_of = [&](int pos) -> int {
+        const int pi = pos < 0 ? 0 : pos / p.page_size;
+        return p.page_table[(int64_t)b * p.max_pages + pi];
+    };
+    auto offset_of = [&](int pos, int pg) -> int64_t {
+        return (pos >= 0 && pg >= 0 && pg < p.num_pages)
+                   ? ((int64_t)pg * p.page_size + pos % p.page_size) * kRec : int64_t(-1);
+    };
+    // masked tokens load record 0 (always present) and are zeroed at dequant
+    auto load = [&](Staged& st, int64_t off) {
+        const uint8_t* rp = cache + (off < 0 ? 0 : off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st.c[k] = *reinterpret_cast<const u32x4*>(rp + 64 * gq + 16 * k);
+        st.sc = *reinterpret_cast<const u32x2*>(rp + 256 + 8 * gq);
+        if (kRopeFp8) {
+            st.r[0] = *reinterpret_cast<const u32x4*>(rp + 288 + 16 * gq);
+            st.r[1] = st.r[0];
+        } else {
+            st.r[0] = *reinterpret_cast<const u32x4*>(rp + 288 + 32 * gq);
+            st.r[1] = *reinterpret_cast<const u32x4*>(rp + 288 + 32 * gq + 16);
+        }
+    };
+
+    f32x4 o[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    _Float16* vt = sm.vt[w];
+
+    auto compute = [&](const Staged& st, int64_t off) {
+        const bool valid = off >= 0;
+        // validity of tokens 0..15 of the tile (lane c16 of group 0 has token c16)
+        const uint32_t vm = (uint32_t)__ballot(valid && gq == 0) & 0xffffu;
+        // ---- S^T: RoPE k-steps (bf16), then the latent ones (fp16)
+        f32x4 s_r = {0.f, 0.f, 0.f, 0.f}, s_l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kr = 0; kr < 2; ++kr) {
+            u32x4 a;
+            if (kRopeFp8) {
+                const uint32_t x0 = st.r[0][2 * kr], x1 = st.r[0][2 * kr + 1];
+                a = u32x4{pack_bf16_exact(e4m3_decode(x0 & 0xffu), e4m3_decode((x0 >> 8) & 0xffu)),
+                          pack_bf16_exact(e4m3_decode((x0 >> 16) & 0xffu), e4m3_decode(x0 >> 24)),
+                          pack_bf16_exact(e4m3_decode(x1 & 0xffu), e4m3_decode((x1 >> 8) & 0xffu)),
+                          pack_bf16_exact(e4m3_decode((x1 >> 16) & 0xffu), e4m3_decode(x1 >> 24))};
+            } else {
+                a = st.r[kr];
+            }
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            s_r = mfma16x16x32(as_bf16x8(valid ? a : zero), qr[kr], s_r);
+        }
+        // the lane's 8 block scales (e4m3 -> fp32 by the hardware FP8
+        // conversion, exact); a masked token gets scale 0, hence zero K and V
+        const uint32_t sw0 = valid ? st.sc[0] : 0u, sw1 = valid ? st.sc[1] : 0u;
+        const f32x2 sf[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(sw0, false), __builtin_amdgcn_cvt_pk_f32_fp8(sw0, true),
+                             __builtin_amdgcn_cvt_pk_f32_fp8(sw1, false), __builtin_amdgcn_cvt_pk_f32_fp8(sw1, true)};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const uint32_t cw = st.c[kk >> 2][kk & 3];
+            const _Float16 sv = (_Float16)sf[kk >> 2][(kk >> 1) & 1];
+            const f16x2 ss = {sv, sv};
+            f16x8 a;
+            const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss;
+            const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss;
+            const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss;
+            const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss;
+            a[0] = v0[0]; a[1] = v0[1]; a[2] = v1[0]; a[3] = v1[1];
+            a[4] = v2[0]; a[5] = v2[1]; a[6] = v3[0]; a[7] = v3[1];
+            s_l = mfma_k32_f16(a, qf[kk], s_l);
+            *reinterpret_cast<f16x8*>(&vt[c16 * kVP + 128 * gq + 8 * kk]) = a;
+        }
+        // ---- online softmax: element i is token 4gq + i of head c16
+        float z[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = ((vm >> (4 * gq + i)) & 1u) ? sc_lat * s_l[i] + sc_rope * s_r[i] : -INFINITY;
+            mx = fmaxf(mx, z[i]);
+        }
+        mx = xor32_max(xor16_max(mx));
+        const bool move = mx > m_run + kRescaleSlack;
+        const float m_new = move ? mx : m_run;
+        const bool live = m_new != -INFINITY;
+        const float alpha = (move && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = live ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.0f;
+            psum += z[i];
+        }
+        psum = xor32_sum(xor16_sum(psum));
+        l_run = alpha * l_run + psum;
+        m_run = m_new;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int c = 0; c < 32; ++c) o[c] *= alpha;
+        }
+        // P as fp16 hi + lo; B operand: head c16, k-slots = tokens 4gq .. +3
+        f16x4 ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ph[i] = (_Float16)z[i];
+            pl[i] = (_Float16)(z[i] - (float)ph[i]);
+        }
+        // ---- O^T = V^T P^T: A fragment of dim tile c by a transposing read;
+        // in each 16-lane group lane s addresses token 4gq + s/4, dims
+        // 16c + 4(s%4) .. +3, and receives the 4 tokens of dim 16c + s.
+        const _Float16* vb = vt + (4 * gq + (c16 >> 2)) * kVP + 4 * (c16 & 3);
+        auto vfrag = [&](int c) {
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+                const_cast<__attribute__((address_space(3))) _Float16*>(
+                    (__attribute__((address_space(3))) const _Float16*)(vb + 16 * c))));
+            return __builtin_bit_cast(f16x4, x);
+        };
+#pragma unroll
+        for (int c = 0; c < 32; c += 2) {
+            const f16x4 va = vfrag(c), vb2 = vfrag(c + 1);
+            o[c] = mfma_k16_f16(va, ph, o[c]);
+            o[c + 1] = mfma_k16_f16(vb2, ph, o[c + 1]);
+            o[c] = mfma_k16_f16(va, pl, o[c]);
+            o[c + 1] = mfma_k16_f16(vb2, pl, o[c + 1]);
+        }
+    };
+
+    // ---- token loop: records of tiles j+1 and j+2 in flight, page-table
+    // entry of tile j+3 loading, index of tile j+4 loading (sparse)
+    if (nmine > 0) {
+        Staged s0, s1, s2;
+        int64_t offA, offB, offC;
+        {
+            const int p0 = position_of(0), p1 = position_of(1), p2 = position_of(2);
+            offA = offset_of(p0, page_of(p0));
+            offB = offset_of(p1, page_of(p1));
+            offC = offset_of(p2, page_of(p2));
+        }
+        load(s0, offA);
+        load(s1, offB);
+        int pos3 = position_of(3);
+        for (int j = 0; j < nmine; ++j) {
+            const int pg3 = page_of(pos3);            // tile j+3, used at the end
+            const int pos4 = position_of(j + 4);
+            load(s2, offC);                            // tile j+2 (masked reloads past the end)
+            compute(s0, offA);
+            const int64_t offD = offset_of(pos3, pg3);
+            s0 = s1;
+            s1 = s2;
+            offA = offB;
+            offB = offC;
+            offC = offD;
+            pos3 = pos4;
+        }
+    }
+
+    // ---- merge the four wavefronts: weights 2^(m_w - M) per head
+    if (gq == 0) {
+        sm.m[w][c16] = m_run;
+        sm.l[w][c16] = l_run;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kNW; ++v) M = fmaxf(M, sm.m[v][c16]);
+    float ltot = 0.0f, aw = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kNW; ++v) {
+        const float mv = sm.m[v][c16];
+        const float a = (mv == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+        ltot += a * sm.l[v][c16];
+        if (v == w) aw = a;
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) o[c] *= aw;
+    // sum of the four O's through LDS (f32x4 per (dim tile, lane))
+    f32x4* area = reinterpret_cast<f32x4*>(&sm.vt[0][0]);   // 2 x 32 KB
+    __syncthreads();
+    if (w >= 2) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) area[(w - 2) * 2048 + c * 64 + lane] = o[c];
+    }
+    __syncthreads();
+    if (w < 2) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) o[c] += area[w * 2048 + c * 64 + lane];
+    }
+    __syncthreads();
+    if (w == 1) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) area[c * 64 + lane] = o[c];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) o[c] += area[c * 64 + lane];
+
+    const bool any = ltot > 0.0f;
+    const float so = any ? outer / ltot : 0.0f;
+    const float lse_v = any ? (M + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+    if (!hok) return;
+    // element i of o[c]: dim 16c + 4gq + i of head c16
+    float* dst;
+    if (ns == 1) {
+        dst = p.out + ((int64_t)b * p.H + c16) * kLatent;
+        if (gq == 0) p.lse[(int64_t)b * p.H + c16] = lse_v;
+    } else {
+        const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + c16;
+        dst = p.ws_out + row * kLatent;
+        if (gq == 0) p.ws_lse[row] = lse_v;
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+}
+
+template <bool kRopeFp8, bool kSparse>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_narrow_kernel<kRopeFp8, kSparse>), dim3((unsigned)a.max_splits, (unsigned)a.B),
+                       dim3(kNW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_narrow(const DecodeArgs& a, hipStream_t stream) {
+    const bool fp8 = a.record_bytes == 368;
+    if (a.indices) return fp8 ? launch_t<true, true>(a, stream) : launch_t<false, true>(a, stream);
+    return fp8 ? launch_t<true, false>(a, stream) : launch_t<false, false>(a, stream);
+}
+
+}  // namespace mla

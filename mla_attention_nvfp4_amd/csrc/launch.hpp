@@ -36,6 +36,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_narrow(const DecodeArgs& a, hipStream_t stream);   // H <= 16
 
 // n = splits_per_seq[b] clamped to [0, S], or S if the pointer is null.
 struct MergeArgs {
