@@ -206,7 +206,7 @@ void decode_kernel(DecodeArgs p) {
             const int tok = kRpw * w + r;
             const bool valid = (vmask >> tok) & 1u;
             const uint32_t c = valid ? rc[r] : 0u;
-            const float sc = e4m3_decode(valid ? rs[r] : 0u);
+            const float sc = e4m3_hw<0>(valid ? rs[r] : 0u);
             const f32x2 v0 = e2m1_pair<0>(c), v1 = e2m1_pair<1>(c);
             const f32x2 v2 = e2m1_pair<2>(c), v3 = e2m1_pair<3>(c);
             const u32x4 wv = {pack_bf16_exact(v0[0] * sc, v0[1] * sc), pack_bf16_exact(v1[0] * sc, v1[1] * sc),
@@ -221,9 +221,9 @@ void decode_kernel(DecodeArgs p) {
             if (kRopeFp8) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const uint32_t x = rr[j];
-                    wv[2 * j] = pack_bf16_exact(e4m3_decode(x & 0xffu), e4m3_decode((x >> 8) & 0xffu));
-                    wv[2 * j + 1] = pack_bf16_exact(e4m3_decode((x >> 16) & 0xffu), e4m3_decode(x >> 24));
+                    const u32x2 y = e4m3x4_to_bf16(rr[j]);
+                    wv[2 * j] = y[0];
+                    wv[2 * j + 1] = y[1];
                 }
             } else {
                 wv = rr;

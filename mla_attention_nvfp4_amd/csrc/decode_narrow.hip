@@ -200,16 +200,15 @@ void decode_narrow_kernel(DecodeArgs p) {
         // validity of tokens 0..15 of the tile (lane c16 of group 0 has token c16)
         const uint32_t vm = (uint32_t)__ballot(valid && gq == 0) & 0xffffu;
         // ---- S^T: RoPE k-steps (bf16), then the latent ones (fp16)
-        f32x4 s_r = {0.f, 0.f, 0.f, 0.f}, s_l = {0.f, 0.f, 0.f, 0.f};
+        // (latent k-steps alternate between two accumulators)
+        f32x4 s_r = {0.f, 0.f, 0.f, 0.f}, s_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kr = 0; kr < 2; ++kr) {
             u32x4 a;
             if (kRopeFp8) {
                 const uint32_t x0 = st.r[0][2 * kr], x1 = st.r[0][2 * kr + 1];
-                a = u32x4{pack_bf16_exact(e4m3_decode(x0 & 0xffu), e4m3_decode((x0 >> 8) & 0xffu)),
-                          pack_bf16_exact(e4m3_decode((x0 >> 16) & 0xffu), e4m3_decode(x0 >> 24)),
-                          pack_bf16_exact(e4m3_decode(x1 & 0xffu), e4m3_decode((x1 >> 8) & 0xffu)),
-                          pack_bf16_exact(e4m3_decode((x1 >> 16) & 0xffu), e4m3_decode(x1 >> 24))};
+                const u32x2 y0 = e4m3x4_to_bf16(x0), y1 = e4m3x4_to_bf16(x1);
+                a = u32x4{y0[0], y0[1], y1[0], y1[1]};
             } else {
                 a = st.r[kr];
             }
@@ -233,7 +232,7 @@ void decode_narrow_kernel(DecodeArgs p) {
             const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss;
             a[0] = v0[0]; a[1] = v0[1]; a[2] = v1[0]; a[3] = v1[1];
             a[4] = v2[0]; a[5] = v2[1]; a[6] = v3[0]; a[7] = v3[1];
-            s_l = mfma_k32_f16(a, qf[kk], s_l);
+            s_l[kk & 1] = mfma_k32_f16(a, qf[kk], s_l[kk & 1]);
             *reinterpret_cast<f16x8*>(&vt[c16 * kVP + 128 * gq + 8 * kk]) = a;
         }
         // ---- online softmax: element i is token 4gq + i of head c16
@@ -241,7 +240,7 @@ void decode_narrow_kernel(DecodeArgs p) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = ((vm >> (4 * gq + i)) & 1u) ? sc_lat * s_l[i] + sc_rope * s_r[i] : -INFINITY;
+            z[i] = ((vm >> (4 * gq + i)) & 1u) ? sc_lat * (s_l[0][i] + s_l[1][i]) + sc_rope * s_r[i] : -INFINITY;
             mx = fmaxf(mx, z[i]);
         }
         mx = xor32_max(xor16_max(mx));
@@ -279,13 +278,16 @@ void decode_narrow_kernel(DecodeArgs p) {
                     (__attribute__((address_space(3))) const _Float16*)(vb + 16 * c))));
             return __builtin_bit_cast(f16x4, x);
         };
+        // all 32 fragments first (one LDS round trip), then the products
+        f16x4 vf[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) vf[c] = vfrag(c);
 #pragma unroll
         for (int c = 0; c < 32; c += 2) {
-            const f16x4 va = vfrag(c), vb2 = vfrag(c + 1);
-            o[c] = mfma_k16_f16(va, ph, o[c]);
-            o[c + 1] = mfma_k16_f16(vb2, ph, o[c + 1]);
-            o[c] = mfma_k16_f16(va, pl, o[c]);
-            o[c + 1] = mfma_k16_f16(vb2, pl, o[c + 1]);
+            o[c] = mfma_k16_f16(vf[c], ph, o[c]);
+            o[c + 1] = mfma_k16_f16(vf[c + 1], ph, o[c + 1]);
+            o[c] = mfma_k16_f16(vf[c], pl, o[c]);
+            o[c + 1] = mfma_k16_f16(vf[c + 1], pl, o[c + 1]);
         }
     };
 

@@ -54,6 +54,19 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
     return (b & 0x80u) ? -v : v;
 }
 
+// fp32 value of e4m3 byte `sel` of x by the gfx950 FP8 conversion (OCP
+// E4M3FN; equal to e4m3_decode for every code the encoders produce), and
+// four such bytes as two packed bf16 pairs (exact: e4m3 fits bf16).
+template <int kSel>
+__device__ __forceinline__ float e4m3_hw(uint32_t x) {
+    return __builtin_amdgcn_cvt_f32_fp8(x, kSel);
+}
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+    return u32x2{__builtin_amdgcn_perm(f2u(lo[1]), f2u(lo[0]), 0x07060302u),
+                 __builtin_amdgcn_perm(f2u(hi[1]), f2u(hi[0]), 0x07060302u)};
+}
+
 // ---------------------------------------------------------------- e2m1 --
 
 // e2m1 code of an fp32 value: RNE, saturating at 6, sign bit kept.  The code
