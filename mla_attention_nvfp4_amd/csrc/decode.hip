@@ -64,31 +64,7 @@ struct DecodeSmem {
     uint32_t valid[kRing];                // bit i: token i of the tile is unmasked
 };
 
-// op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]) by the gfx950 row-swap
-// permutes (each returns {x[l], x[l ^ 16 or 32]} in some order).
-__device__ __forceinline__ float xor16_max(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    return u2f(r[0]) + u2f(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return u2f(r[0]) + u2f(r[1]);
-}
 
-// LDS-only workgroup barrier: this wavefront's LDS operations are complete
-// before it arrives; outstanding global loads stay in flight.  (The asm's
-// memory clobber keeps the compiler from moving memory accesses across.)
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 
 template <int NW, bool kRopeFp8, bool kSparse>

@@ -64,22 +64,6 @@ __device__ __forceinline__ f32x4 mfma_k16_f16(f16x4 a, f16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor16_max(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    return u2f(r[0]) + u2f(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return u2f(r[0]) + u2f(r[1]);
-}
 
 // The record bytes one lane needs for its token: 64 code bytes, 8 scale
 // bytes, and its RoPE share (32 B bf16 or 16 B e4m3).

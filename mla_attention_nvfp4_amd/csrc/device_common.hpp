@@ -29,34 +29,27 @@ __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
 // ---------------------------------------------------------------- e4m3 --
 
 // e4m3 code of an fp32 value: RNE, satfinite (|t| >= 448 -> 0x7E), sign kept.
+// Branch-free: the three cases are computed and selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
     const uint32_t bits = f2u(t);
     const uint32_t sign = (bits >> 24) & 0x80u;
     const uint32_t a = bits & 0x7fffffffu;
-    uint32_t code;
-    if (a >= 0x43e00000u) {               // >= 448.0f (and inf)
-        code = 0x7eu;
-    } else if (a < 0x3c800000u) {         // < 2^-6: multiples of 2^-9
-        code = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);   // exact scaling, RNE
-    } else {                              // normal: round the mantissa to 3 bits
-        const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-        code = r - ((127u - 7u) << 3);
-    }
+    // below 2^-6: multiples of 2^-9 (exact scaling, RNE)
+    const uint32_t sub = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);
+    // normal: round the mantissa to 3 bits, rebias
+    const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    const uint32_t code = a >= 0x43e00000u ? 0x7eu : (a < 0x3c800000u ? sub : nrm);   // >= 448 (and inf)
     return sign | code;
 }
 
-// fp32 value of an e4m3 code (codes 0x7F/0xFF, NaN, are never produced by
-// the encoders here and are not special-cased).
+// fp32 value of an e4m3 code by the gfx950 FP8 conversion (OCP E4M3FN,
+// exact; codes 0x7F/0xFF are NaN and never produced by the encoders here).
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-    const uint32_t m = b & 0x7fu;
-    float v = (m >= 8u) ? u2f((m << 20) + (120u << 23))
-                        : (u2f((m << 20) + (121u << 23)) - 0.015625f);
-    return (b & 0x80u) ? -v : v;
+    return __builtin_amdgcn_cvt_f32_fp8(b & 0xffu, 0);
 }
 
-// fp32 value of e4m3 byte `sel` of x by the gfx950 FP8 conversion (OCP
-// E4M3FN; equal to e4m3_decode for every code the encoders produce), and
-// four such bytes as two packed bf16 pairs (exact: e4m3 fits bf16).
+// fp32 value of e4m3 byte `sel` of x (as e4m3_decode), and four such bytes
+// as two packed bf16 pairs (exact: e4m3 fits bf16).
 template <int kSel>
 __device__ __forceinline__ float e4m3_hw(uint32_t x) {
     return __builtin_amdgcn_cvt_f32_fp8(x, kSel);
@@ -159,6 +152,32 @@ __device__ __forceinline__ float wave_xor_max(float v, int mask) {
 }
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
     return v + __shfl_xor(v, mask, 64);
+}
+
+// op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]) by the gfx950 row-swap
+// permutes (VALU; each returns {x[l], x[l ^ 16 or 32]} in some order).
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+
+// LDS-only workgroup barrier: this wavefront's LDS operations are complete
+// before it arrives; outstanding global loads stay in flight.  (The asm's
+// memory clobber keeps the compiler from moving memory accesses across.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace mla

@@ -132,9 +132,10 @@ struct AttnParams {
     int H;
     float score_scale_log2;   // softmax_scale * g_q' * g_k' * log2(e)
     double out_scale;         // g_p' * g_v' (exact in fp64)
-    float g_p;                // P multiplier (only used when quantize_p)
+    float g_p;                // P multiplier (P quantized only)
+    float u_p;                // fp32(6 g_p)
+    float inv_u_p;            // fp32(1 / u_p)
     float g_out;              // output global scale
-    int quantize_p;
     int64_t T;
     uint8_t* out_fp4;
     uint8_t* out_scales;
@@ -144,7 +145,20 @@ struct AttnParams {
 struct AttnSmem {
     uint16_t kt[2][kBN * kPitch];   // 2 x 26624 B
     uint16_t vt[2][kBN * kPitch];   // 2 x 26624 B
+    float pinv[256];                // P block scale code -> fp32(1 / fp32(e4m3(code) g_p)), 0 for d = 0
 };
+
+// e4m3 code of a P block with amax a >= 0: the quantizer's t = fp32(a / u)
+// by one multiply with fp32(1/u); the product lies within two ulps of the
+// quotient, so the code can differ only when it is within a few ulps of an
+// e4m3 rounding tie (or in the subnormal range, where the rounding is done
+// on t * 512): those lanes redo the exact division.
+__device__ __forceinline__ uint32_t p_scale_code(float a, float u, float inv_u) {
+    const float tq = a * inv_u;
+    const uint32_t rem = f2u(tq) & 0xfffffu;
+    const bool near = tq < 0.015625f || (rem > 0x80000u - 8u && rem < 0x80000u + 8u);
+    return e4m3_encode(near ? a / u : tq);
+}
 
 // Values of the two e2m1 codes in byte kSel of w, unit scale.
 template <int kSel>
@@ -152,9 +166,14 @@ __device__ __forceinline__ f32x2 fp4_pair(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);
 }
 
+template <bool kQuantP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnParams p) {
     __shared__ AttnSmem sm;
+    if (kQuantP && threadIdx.x < 256) {
+        const float d = e4m3_decode(threadIdx.x) * p.g_p;
+        sm.pinv[threadIdx.x] = (d == 0.0f) ? 0.0f : 1.0f / d;
+    }
     const int n = blockIdx.z, h = blockIdx.y;
     const int a = p.cu[n], e = p.cu[n + 1];
     const int L = e - a;
@@ -258,8 +277,7 @@ void attn_kernel(AttnParams p) {
                     z[mt][i] = (key <= row) ? p.score_scale_log2 * s[rg][mt][i] : -INFINITY;
                     mx = fmaxf(mx, z[mt][i]);
                 }
-            mx = wave_xor_max(mx, 16);
-            mx = wave_xor_max(mx, 32);
+            mx = xor32_max(xor16_max(mx));
             const float m_new = fmaxf(m_run[rg], mx);
             const bool live = m_new != -INFINITY;
             alpha[rg] = (m_run[rg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
@@ -272,23 +290,24 @@ void attn_kernel(AttnParams p) {
                     pv[mt][i] = live ? __builtin_amdgcn_exp2f(z[mt][i] - m_new) : 0.0f;
                     psum += pv[mt][i];
                 }
-            psum = wave_xor_sum(psum, 16);
-            psum = wave_xor_sum(psum, 32);
+            psum = xor32_sum(xor16_sum(psum));
             l_run[rg] = alpha[rg] * l_run[rg] + psum;   // unquantized denominator
             m_run[rg] = m_new;
-            if (p.quantize_p) {
+            if constexpr (kQuantP) {
                 // 16-key block = key m-tile mt: amax over its 4 lane groups
+                float am[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    am[mt] = xor32_max(xor16_max(fmaxf(fmaxf(pv[mt][0], pv[mt][1]), fmaxf(pv[mt][2], pv[mt][3]))));
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    float am = fmaxf(fmaxf(pv[mt][0], pv[mt][1]), fmaxf(pv[mt][2], pv[mt][3]));
-                    am = wave_xor_max(am, 16);
-                    am = wave_xor_max(am, 32);
-                    const Nvfp4Scale sc = nvfp4_block_scale(am, p.g_p);
-                    const float sval = e4m3_decode(sc.code);
-                    uint32_t codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[mt][0] * sc.inv,
-                                                                             pv[mt][1] * sc.inv, 1.0f, 0);
-                    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, pv[mt][2] * sc.inv,
-                                                                    pv[mt][3] * sc.inv, 1.0f, 1);
+                    const uint32_t code = p_scale_code(am[mt], p.u_p, p.inv_u_p);
+                    const float inv = sm.pinv[code];
+                    const float sval = e4m3_decode(code);
+                    uint32_t codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[mt][0] * inv,
+                                                                             pv[mt][1] * inv, 1.0f, 0);
+                    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, pv[mt][2] * inv,
+                                                                    pv[mt][3] * inv, 1.0f, 1);
                     const f32x2 d0 = fp4_pair<0>(codes), d1 = fp4_pair<1>(codes);
                     pv[mt][0] = d0[0] * sval;
                     pv[mt][1] = d0[1] * sval;
@@ -310,7 +329,7 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
                     for (int pr = 0; pr < 2; ++pr) {
                         const float x0 = src[2 * pr], x1 = src[2 * pr + 1];
-                        if (p.quantize_p) {
+                        if constexpr (kQuantP) {
                             hv[2 * hh + pr] = pack_bf16_exact(x0, x1);
                             mv[2 * hh + pr] = 0u;
                             lv[2 * hh + pr] = 0u;
@@ -329,10 +348,13 @@ void attn_kernel(AttnParams p) {
                 pl[rg][k2] = as_bf16x8(lv);
             }
         }
+        // (multiplying by 1 changes nothing: skipped when no row moved)
+        if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
+            for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[rg][dt] *= alpha[rg];
+                for (int dt = 0; dt < 8; ++dt) o[rg][dt] *= alpha[rg];
+        }
         // V^T fragments by transposing reads: within each 16-lane group,
         // lane s addresses key 32k2 + 4gq + s/4 (+16 for the second half)
         // and dims 16dt + 4(s%4) .. +3
@@ -351,7 +373,7 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
                 for (int rg = 0; rg < 2; ++rg) {
                     o[rg][dt] = mfma16x16x32(va, ph[rg][k2], o[rg][dt]);
-                    if (!p.quantize_p) {
+                    if constexpr (!kQuantP) {
                         o[rg][dt] = mfma16x16x32(va, pm[rg][k2], o[rg][dt]);
                         o[rg][dt] = mfma16x16x32(va, pl[rg][k2], o[rg][dt]);
                     }
@@ -370,7 +392,7 @@ void attn_kernel(AttnParams p) {
         if (wave_rows && kt * kBN <= wave_last_row) compute(kt, kt & 1);
         if (kt + 1 < nkt) store_tile((kt + 1) & 1);   // staged during compute(kt)
         if (kt + 2 < nkt) load_tile(kt + 2);          // lands during compute(kt+1)
-        __syncthreads();
+        lds_barrier();
     }
 
     if (!wave_rows) return;
@@ -395,8 +417,7 @@ void attn_kernel(AttnParams p) {
                 x[i] = (float)((double)o[rg][dt][i] * inv_l);
                 am = fmaxf(am, __builtin_fabsf(x[i]));
             }
-            am = wave_xor_max(am, 16);
-            am = wave_xor_max(am, 32);
+            am = xor32_max(xor16_max(am));
             const Nvfp4Scale sc = nvfp4_block_scale(am, p.g_out);
             const uint32_t c2 = e2m1_encode(x[0] * sc.inv) | (e2m1_encode(x[1] * sc.inv) << 4) |
                                 (e2m1_encode(x[2] * sc.inv) << 8) | (e2m1_encode(x[3] * sc.inv) << 12);
@@ -471,15 +492,19 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.score_scale_log2 = a.softmax_scale * gq * gk * kLog2e;
     p.out_scale = (double)gp * (double)gv;
     p.g_p = a.g_p;
+    p.u_p = 6.0f * a.g_p;
+    p.inv_u_p = 1.0f / p.u_p;
     p.g_out = a.g_out;
-    p.quantize_p = (a.flags & 4u) ? 1 : 0;
     p.T = T;
     p.out_fp4 = a.out_fp4;
     p.out_scales = a.out_scales;
     p.lse = a.lse;
     if (a.max_seqlen > 0) {
         const dim3 grid((unsigned)((a.max_seqlen + kBM - 1) / kBM), (unsigned)H, (unsigned)a.N);
-        hipLaunchKernelGGL(attn_kernel, grid, dim3(kWaves * 64), 0, stream, p);
+        if (a.flags & 4u)
+            hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kWaves * 64), 0, stream, p);
+        else
+            hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kWaves * 64), 0, stream, p);
     }
     const int64_t cpad = (int64_t)H * 8;
     const int64_t npad = ((T + 127) / 128 * 128 - T) * cpad;
