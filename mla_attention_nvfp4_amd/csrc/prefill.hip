@@ -89,6 +89,10 @@ __global__ __launch_bounds__(256) void qk_qdq_kernel(const uint16_t* __restrict_
 // ------------------------------------------------------------------- V --
 
 // grid (ceil(max_seqlen/16), N, ceil(H*128/256)); thread = (head, dim)
+// kF16Out: the exact values s*v are written as fp16 (they fit: at most 6
+// significant bits, magnitudes in [2^-10, 2688]) for the fp16 PV products,
+// otherwise as bf16.
+template <bool kF16Out>
 __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__ v, int64_t st, int64_t sh,
                                                     const int32_t* __restrict__ cu, int H, float g,
                                                     uint16_t* __restrict__ out) {
@@ -117,7 +121,8 @@ __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__
     for (int i = 0; i < 16; ++i) {
         if (i < cnt) {
             const float q = e2m1_decode(e2m1_encode(x[i] * sc.inv)) * sv;
-            out[((int64_t)(t0 + i) * H + h) * kDv + d] = (uint16_t)(f2u(q) >> 16);
+            out[((int64_t)(t0 + i) * H + h) * kDv + d] =
+                kF16Out ? __builtin_bit_cast(uint16_t, (_Float16)q) : (uint16_t)(f2u(q) >> 16);
         }
     }
 }
@@ -160,13 +165,39 @@ __device__ __forceinline__ uint32_t p_scale_code(float a, float u, float inv_u) 
     return e4m3_encode(near ? a / u : tq);
 }
 
-// Values of the two e2m1 codes in byte kSel of w, unit scale.
-template <int kSel>
-__device__ __forceinline__ f32x2 fp4_pair(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// D = A (32x16) * B (16x32) + C, fp32 accumulate.  Lane l supplies row
+// l % 32 of A and column l % 32 of B with k-slots 8(l/32) .. +7; it receives
+// D[8(v/4) + 4(l/32) + v%4][l % 32] in element v.
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <bool kQuantP>
+template <bool V>
+struct BoolTag {
+    static constexpr bool value = V;
+};
+
+// Layout of a wavefront's work on one 64-key tile (32 query rows): lane l
+// owns query row l % 32 (g2 = l / 32 picks half of the keys).  Score tile
+// mt2 = S^T for keys 32 mt2 .. +31; its element v is key 32 mt2 + 8(v/4) +
+// 4 g2 + v%4.  So the 16-key P block kb (keys 16kb .. +15) is elements
+// 8(kb%2) .. +7 of tile kb/2 in lanes l and l ^ 32, and those 8 values, in
+// order, are also the k-slots of k-step kb of the B operand of O^T = V^T P^T
+// (slot j <-> key 16kb + 8(j/4) + 4 g2 + j%4; the V^T operand uses the same
+// slots).
+//
+// kF16: P and V are both quantized, so P^ = s*v and V^ = s*v are exact in
+// fp16 and the PV products run in fp16, P^ coming straight from the FP4
+// conversion; otherwise they run in bf16 (quantized P exact, unquantized P
+// split into three bf16 parts).
+template <bool kQuantP, bool kF16>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnParams p) {
     __shared__ AttnSmem sm;
@@ -182,18 +213,18 @@ void attn_kernel(AttnParams p) {
     if (qt < 0) return;
     const int r0 = qt * kBM;                     // local row of the tile
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int gq = lane >> 4, c16 = lane & 15;
+    const int l32 = lane & 31, g2 = lane >> 5;
     const int wr0 = r0 + kRowsPerWave * w;       // first local row of this wavefront
     const bool wave_rows = wr0 < L;
+    const int row = wr0 + l32;                   // this lane's query row
 
-    // Q rows of the wavefront: B operand of S^T = K Q^T (2 row groups of 16)
-    bf16x8 qf[2][6];
+    // Q row (B operand of S^T = K Q^T): k-step kk covers dims 16kk + 8 g2 .. +7
+    bf16x8 qf[12];
+    {
+        const int rr = min(row, L - 1);
+        const uint16_t* src = p.q + (int64_t)(a + rr) * p.q_st + (int64_t)h * p.q_sh + 8 * g2;
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-        const int row = min(wr0 + 16 * rg + c16, L - 1);
-        const uint16_t* src = p.q + (int64_t)(a + row) * p.q_st + (int64_t)h * p.q_sh + 8 * gq;
-#pragma unroll
-        for (int kk = 0; kk < 6; ++kk) qf[rg][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * kk));
+        for (int kk = 0; kk < 12; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * kk));
     }
 
     // last key tile this workgroup needs; a wavefront needs tiles up to its last row
@@ -207,16 +238,14 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             const int c = tid + 512 * i;
-            const int row = c / 24, col = c % 24;
-            const int j = min(kt * kBN + row, L - 1);
-            sk[i] = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(a + j) * p.k_st + (int64_t)h * p.k_sh + 8 * col);
+            const int j = min(kt * kBN + c / 24, L - 1);
+            sk[i] = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(a + j) * p.k_st + (int64_t)h * p.k_sh + 8 * (c % 24));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 512 * i;
-            const int row = c >> 4, col = c & 15;
-            const int j = min(kt * kBN + row, L - 1);
-            sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(a + j) * p.v_st + (int64_t)h * p.v_sh + 8 * col);
+            const int j = min(kt * kBN + (c >> 4), L - 1);
+            sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(a + j) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15));
         }
     };
     auto store_tile = [&](int buf) {
@@ -232,150 +261,140 @@ void attn_kernel(AttnParams p) {
         }
     };
 
-    f32x4 o[2][8];
+    f32x16 o[4];   // O^T: element v of o[dt] is dim 32dt + 8(v/4) + 4 g2 + v%4 of this row
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[rg][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float c_log2 = p.score_scale_log2;
 
-    auto compute = [&](int kt, int buf) {
+    auto compute = [&](int kt, int buf, auto mask_tag) {
+        constexpr bool kMask = decltype(mask_tag)::value;
         const uint16_t* kb = sm.kt[buf];
         const uint16_t* vb = sm.vt[buf];
-        // S^T [64 keys x 32 rows]: 4 key m-tiles x 2 row groups
-        f32x4 s[2][4];
+        // ---- S^T for keys 32 mt2 .. +31
+        f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
+        for (int kk = 0; kk < 12; ++kk) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) s[rg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 6; ++kk) {
-            u32x4 af[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                af[mt] = *reinterpret_cast<const u32x4*>(&kb[(16 * mt + c16) * kPitch + 32 * kk + 8 * gq]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int rg = 0; rg < 2; ++rg) s[rg][mt] = mfma16x16x32(as_bf16x8(af[mt]), qf[rg][kk], s[rg][mt]);
+            for (int mt2 = 0; mt2 < 2; ++mt2) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(&kb[(32 * mt2 + l32) * kPitch + 16 * kk + 8 * g2]);
+                s[mt2] = mfma32_bf16(as_bf16x8(af), qf[kk], s[mt2]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // softmax + P quantization per row group; lane holds keys
-        // 16mt + 4gq + i (local in the tile) of row wr0 + 16rg + c16
-        bf16x8 ph[2][2], pm[2][2], pl[2][2];
-        float alpha[2];
+        // ---- softmax: z in log2 units; the running max refreshed per tile
+        float mx = -INFINITY;
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-            const int row = wr0 + 16 * rg + c16;
-            float z[4][4];
-            float mx = -INFINITY;
+        for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kt * kBN + 16 * mt + 4 * gq + i;
-                    z[mt][i] = (key <= row) ? p.score_scale_log2 * s[rg][mt][i] : -INFINITY;
-                    mx = fmaxf(mx, z[mt][i]);
+            for (int v = 0; v < 16; ++v) {
+                float z = c_log2 * s[mt2][v];
+                if (kMask) {
+                    const int key = kt * kBN + 32 * mt2 + 8 * (v >> 2) + 4 * g2 + (v & 3);
+                    z = key <= row ? z : -INFINITY;
                 }
-            mx = xor32_max(xor16_max(mx));
-            const float m_new = fmaxf(m_run[rg], mx);
-            const bool live = m_new != -INFINITY;
-            alpha[rg] = (m_run[rg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
-            float pv[4][4];
-            float psum = 0.0f;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[mt][i] = live ? __builtin_amdgcn_exp2f(z[mt][i] - m_new) : 0.0f;
-                    psum += pv[mt][i];
-                }
-            psum = xor32_sum(xor16_sum(psum));
-            l_run[rg] = alpha[rg] * l_run[rg] + psum;   // unquantized denominator
-            m_run[rg] = m_new;
-            if constexpr (kQuantP) {
-                // 16-key block = key m-tile mt: amax over its 4 lane groups
-                float am[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    am[mt] = xor32_max(xor16_max(fmaxf(fmaxf(pv[mt][0], pv[mt][1]), fmaxf(pv[mt][2], pv[mt][3]))));
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const uint32_t code = p_scale_code(am[mt], p.u_p, p.inv_u_p);
-                    const float inv = sm.pinv[code];
-                    const float sval = e4m3_decode(code);
-                    uint32_t codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[mt][0] * inv,
-                                                                             pv[mt][1] * inv, 1.0f, 0);
-                    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, pv[mt][2] * inv,
-                                                                    pv[mt][3] * inv, 1.0f, 1);
-                    const f32x2 d0 = fp4_pair<0>(codes), d1 = fp4_pair<1>(codes);
-                    pv[mt][0] = d0[0] * sval;
-                    pv[mt][1] = d0[1] * sval;
-                    pv[mt][2] = d1[0] * sval;
-                    pv[mt][3] = d1[1] * sval;
-                }
+                s[mt2][v] = z;
+                mx = fmaxf(mx, z);
             }
-            // B operand of O^T = V^T P^T, k-step k2 (keys 32k2 .. +31): slot
-            // j < 4 is key 32k2 + 4gq + j (m-tile 2k2), j >= 4 is key
-            // 32k2 + 16 + 4gq + j - 4 (m-tile 2k2 + 1).  Quantized P is
-            // exact in bf16; unquantized P is split into three bf16 parts
-            // (|p - hi - mid - lo| <= 2^-24 |p|).
+        mx = xor32_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        float psum = 0.0f;
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
+        for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[mt2][v] = __builtin_amdgcn_exp2f(s[mt2][v] - m_use);
+                psum += s[mt2][v];
+            }
+        psum = xor32_sum(psum);
+        l_run = alpha * l_run + psum;   // unquantized denominator
+        m_run = m_new;
+        // (multiplying by 1 changes nothing: skipped when no row moved)
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        }
+        // ---- P operands per 16-key block kb
+        f16x8 pf[4];
+        bf16x8 ph[4], pm[4], pl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = s[kb >> 1][8 * (kb & 1) + i];
+            if constexpr (kQuantP) {
+                float am = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                am = xor32_max(am);
+                const uint32_t code = p_scale_code(am, p.u_p, p.inv_u_p);
+                const float inv = sm.pinv[code];
+                const float sval = e4m3_decode(code);
+                uint32_t c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0] * inv, x[1] * inv, 1.0f, 0);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[2] * inv, x[3] * inv, 1.0f, 1);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[4] * inv, x[5] * inv, 1.0f, 2);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[6] * inv, x[7] * inv, 1.0f, 3);
+                if constexpr (kF16) {
+                    const _Float16 sh = (_Float16)sval;
+                    const f16x2 ss = {sh, sh};
+                    const f16x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 0) * ss;
+                    const f16x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 1) * ss;
+                    const f16x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 2) * ss;
+                    const f16x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 3) * ss;
+                    pf[kb] = f16x8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+                } else {
+                    const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 0);
+                    const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 1);
+                    const f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 2);
+                    const f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 3);
+                    ph[kb] = as_bf16x8(u32x4{pack_bf16_exact(d0[0] * sval, d0[1] * sval),
+                                             pack_bf16_exact(d1[0] * sval, d1[1] * sval),
+                                             pack_bf16_exact(d2[0] * sval, d2[1] * sval),
+                                             pack_bf16_exact(d3[0] * sval, d3[1] * sval)});
+                }
+            } else {
+                // three bf16 parts (|p - hi - mid - lo| <= 2^-24 |p|)
                 u32x4 hv, mv, lv;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float* src = pv[2 * k2 + hh];
-#pragma unroll
-                    for (int pr = 0; pr < 2; ++pr) {
-                        const float x0 = src[2 * pr], x1 = src[2 * pr + 1];
-                        if constexpr (kQuantP) {
-                            hv[2 * hh + pr] = pack_bf16_exact(x0, x1);
-                            mv[2 * hh + pr] = 0u;
-                            lv[2 * hh + pr] = 0u;
-                        } else {
-                            const uint32_t h1 = pack_bf16_rne(x0, x1);
-                            const float r0 = x0 - bf16_lo(h1), r1 = x1 - bf16_hi(h1);
-                            const uint32_t m1 = pack_bf16_rne(r0, r1);
-                            hv[2 * hh + pr] = h1;
-                            mv[2 * hh + pr] = m1;
-                            lv[2 * hh + pr] = pack_bf16_rne(r0 - bf16_lo(m1), r1 - bf16_hi(m1));
-                        }
-                    }
+                for (int pr = 0; pr < 4; ++pr) {
+                    const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+                    const uint32_t h1 = pack_bf16_rne(x0, x1);
+                    const float e0 = x0 - bf16_lo(h1), e1 = x1 - bf16_hi(h1);
+                    const uint32_t m1 = pack_bf16_rne(e0, e1);
+                    hv[pr] = h1;
+                    mv[pr] = m1;
+                    lv[pr] = pack_bf16_rne(e0 - bf16_lo(m1), e1 - bf16_hi(m1));
                 }
-                ph[rg][k2] = as_bf16x8(hv);
-                pm[rg][k2] = as_bf16x8(mv);
-                pl[rg][k2] = as_bf16x8(lv);
+                ph[kb] = as_bf16x8(hv);
+                pm[kb] = as_bf16x8(mv);
+                pl[kb] = as_bf16x8(lv);
             }
         }
-        // (multiplying by 1 changes nothing: skipped when no row moved)
-        if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+        // ---- O^T += V^T P^T.  A fragment (dim tile dt, k-step kb): lane l
+        // gets dim 32dt + l%32 and keys 16kb + 4 g2 + 0..3 (slots 0..3) and
+        // 16kb + 8 + 4 g2 + 0..3 (slots 4..7) by two transposing reads; in each
+        // 16-lane group lane s addresses key row k0 + s/4 and dims c0 + 4(s%4)
+        // .. +3, and receives the 4 keys of dim c0 + s.
+        const int s16 = lane & 15;
+        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitch + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
 #pragma unroll
-            for (int rg = 0; rg < 2; ++rg)
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[rg][dt] *= alpha[rg];
-        }
-        // V^T fragments by transposing reads: within each 16-lane group,
-        // lane s addresses key 32k2 + 4gq + s/4 (+16 for the second half)
-        // and dims 16dt + 4(s%4) .. +3
-        const uint16_t* vbase = vb + (4 * gq + (c16 >> 2)) * kPitch + 4 * (c16 & 3);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const uint16_t* p1 = vbase + 32 * k2 * kPitch + 16 * dt;
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint16_t* a0 = vbase + 16 * kb * kPitch + 32 * dt;
                 const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(p1)));
+                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
                 const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(p1 + 16 * kPitch)));
+                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitch)));
                 const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-                const bf16x8 va = as_bf16x8(u32x4{y1[0], y1[1], y2[0], y2[1]});
-#pragma unroll
-                for (int rg = 0; rg < 2; ++rg) {
-                    o[rg][dt] = mfma16x16x32(va, ph[rg][k2], o[rg][dt]);
+                const u32x4 va = u32x4{y1[0], y1[1], y2[0], y2[1]};
+                if constexpr (kF16) {
+                    o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, va), pf[kb], o[dt]);
+                } else {
+                    o[dt] = mfma32_bf16(as_bf16x8(va), ph[kb], o[dt]);
                     if constexpr (!kQuantP) {
-                        o[rg][dt] = mfma16x16x32(va, pm[rg][k2], o[rg][dt]);
-                        o[rg][dt] = mfma16x16x32(va, pl[rg][k2], o[rg][dt]);
+                        o[dt] = mfma32_bf16(as_bf16x8(va), pm[kb], o[dt]);
+                        o[dt] = mfma32_bf16(as_bf16x8(va), pl[kb], o[dt]);
                     }
                 }
             }
@@ -388,50 +407,55 @@ void attn_kernel(AttnParams p) {
     if (nkt > 1) load_tile(1);
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-        // a wavefront skips tiles that start after its last row
-        if (wave_rows && kt * kBN <= wave_last_row) compute(kt, kt & 1);
+        // a wavefront skips tiles that start after its last row; tiles
+        // entirely at or below its first row need no causal mask
+        if (wave_rows && kt * kBN <= wave_last_row) {
+            if (kt * kBN + kBN - 1 <= wr0) compute(kt, kt & 1, BoolTag<false>{});
+            else compute(kt, kt & 1, BoolTag<true>{});
+        }
         if (kt + 1 < nkt) store_tile((kt + 1) & 1);   // staged during compute(kt)
         if (kt + 2 < nkt) load_tile(kt + 2);          // lands during compute(kt+1)
         lds_barrier();
     }
 
     if (!wave_rows) return;
-    // epilogue: lane holds O^T[dim 16dt + 4gq + i][row c16] of row group rg
+    // ---- epilogue: O = acc * g_p g_v / l in fp64, rounded once to fp32 (when
+    // the accumulation is exact, as for a row that sees one key, NVFP4
+    // rounding ties then break as in an exact evaluation); output block b
+    // (dims 16b .. +15) is elements 8(b%2) .. +7 of o[b/2] in lanes l and
+    // l ^ 32: dims 16b + 4 g2 + 0..3 and 16b + 8 + 4 g2 + 0..3.
+    const bool ok = row < L;
+    const double inv_l = l_run > 0.0f ? p.out_scale / (double)l_run : 0.0;
+    const int64_t t = a + row;
+    uint8_t* codes_row = p.out_fp4 + (t * p.H + h) * (kDv / 2);
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-        const int row = wr0 + 16 * rg + c16;
-        const bool ok = row < L;
-        // O = acc * g_p g_v / l in fp64, rounded once to fp32: when the
-        // accumulation is exact (a row that sees one key) this is the
-        // correctly rounded value, so NVFP4 rounding ties break as in an
-        // exact evaluation.
-        const double inv_l = l_run[rg] > 0.0f ? p.out_scale / (double)l_run[rg] : 0.0;
-        const int64_t t = a + row;
-        uint8_t* codes_row = p.out_fp4 + (t * p.H + h) * (kDv / 2);
+    for (int b = 0; b < 8; ++b) {
+        float x[8];
+        float am = 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            float x[4];
-            float am = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = (float)((double)o[rg][dt][i] * inv_l);
-                am = fmaxf(am, __builtin_fabsf(x[i]));
-            }
-            am = xor32_max(xor16_max(am));
-            const Nvfp4Scale sc = nvfp4_block_scale(am, p.g_out);
-            const uint32_t c2 = e2m1_encode(x[0] * sc.inv) | (e2m1_encode(x[1] * sc.inv) << 4) |
-                                (e2m1_encode(x[2] * sc.inv) << 8) | (e2m1_encode(x[3] * sc.inv) << 12);
-            if (ok) {
-                *reinterpret_cast<uint16_t*>(codes_row + 8 * dt + 2 * gq) = (uint16_t)c2;
-                if (gq == 0) {
-                    const int64_t cpad = (int64_t)p.H * 8;
-                    p.out_scales[swizzled_scale_offset(t, (int64_t)h * 8 + dt, cpad)] = (uint8_t)sc.code;
-                }
+        for (int i = 0; i < 8; ++i) {
+            x[i] = (float)((double)o[b >> 1][8 * (b & 1) + i] * inv_l);
+            am = fmaxf(am, __builtin_fabsf(x[i]));
+        }
+        am = xor32_max(am);
+        const Nvfp4Scale sc = nvfp4_block_scale(am, p.g_out);
+        // codes of dims 16b + 4 g2 + 0..3 (bytes 2 g2, 2 g2 + 1) and
+        // 16b + 8 + 4 g2 + 0..3 (bytes 4 + 2 g2, 5 + 2 g2)
+        const uint32_t c01 = e2m1_encode(x[0] * sc.inv) | (e2m1_encode(x[1] * sc.inv) << 4) |
+                             (e2m1_encode(x[2] * sc.inv) << 8) | (e2m1_encode(x[3] * sc.inv) << 12);
+        const uint32_t c23 = e2m1_encode(x[4] * sc.inv) | (e2m1_encode(x[5] * sc.inv) << 4) |
+                             (e2m1_encode(x[6] * sc.inv) << 8) | (e2m1_encode(x[7] * sc.inv) << 12);
+        if (ok) {
+            *reinterpret_cast<uint16_t*>(codes_row + 8 * b + 2 * g2) = (uint16_t)c01;
+            *reinterpret_cast<uint16_t*>(codes_row + 8 * b + 4 + 2 * g2) = (uint16_t)c23;
+            if (g2 == 0) {
+                const int64_t cpad = (int64_t)p.H * 8;
+                p.out_scales[swizzled_scale_offset(t, (int64_t)h * 8 + b, cpad)] = (uint8_t)sc.code;
             }
         }
-        if (ok && gq == 0 && p.lse)
-            p.lse[t * p.H + h] = l_run[rg] > 0.0f ? (m_run[rg] + __builtin_amdgcn_logf(l_run[rg])) * kLn2 : -INFINITY;
     }
+    if (ok && g2 == 0 && p.lse)
+        p.lse[t * p.H + h] = l_run > 0.0f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
 }
 
 // Zero the scale bytes of rows T .. ceil(T/128)*128 - 1 (all columns).
@@ -481,7 +505,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     }
     if (a.flags & 8u) {
         const dim3 grid((unsigned)((a.max_seqlen + 15) / 16), (unsigned)a.N, (unsigned)((H * kDv + 255) / 256));
-        hipLaunchKernelGGL(v_qdq_kernel, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens, H, a.g_v, ws);
+        if (a.flags & 4u)
+            hipLaunchKernelGGL(v_qdq_kernel<true>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens, H,
+                               a.g_v, ws);
+        else
+            hipLaunchKernelGGL(v_qdq_kernel<false>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens,
+                               H, a.g_v, ws);
         p.v = ws; p.v_st = (int64_t)H * kDv; p.v_sh = kDv;
         gv = a.g_v;
         ws += (size_t)T * H * kDv;
@@ -501,10 +530,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.lse = a.lse;
     if (a.max_seqlen > 0) {
         const dim3 grid((unsigned)((a.max_seqlen + kBM - 1) / kBM), (unsigned)H, (unsigned)a.N);
-        if (a.flags & 4u)
-            hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kWaves * 64), 0, stream, p);
+        if ((a.flags & 4u) && (a.flags & 8u))
+            hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kWaves * 64), 0, stream, p);
+        else if (a.flags & 4u)
+            hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kWaves * 64), 0, stream, p);
         else
-            hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kWaves * 64), 0, stream, p);
+            hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kWaves * 64), 0, stream, p);
     }
     const int64_t cpad = (int64_t)H * 8;
     const int64_t npad = ((T + 127) / 128 * 128 - T) * cpad;

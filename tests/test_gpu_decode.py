@@ -18,6 +18,9 @@ SMALL_DENSE = [
     (4, 5, 32, [5, 200, 129, 64, 1], 48, 432, 0.55, 2),
     (5, 2, 64, [2049, 4096], 64, 368, 1.3, 16),
     (6, 1, 1, [77], 8, 432, 1.0, 1),
+    (8, 3, 16, [700, 33, 2000], 16, 368, 1.4, 3),     # narrow heads, e4m3 RoPE, outliers
+    (9, 2, 7, [300, 1029], 48, 432, 0.6, 2),          # narrow, 7 heads
+    (10, 2, 100, [555, 1200], 64, 368, 1.1, 2),       # wide, partial head group
 ]
 
 
@@ -52,6 +55,15 @@ def test_sparse_small(case):
     out, lse = gpu_decode(inp, cache)
     ref_out, ref_lse = oracle_decode(inp, list(range(B)))
     compare(out, lse, ref_out, ref_lse, list(range(B)), f"sparse{seed}")
+
+
+def test_sparse_narrow_fp8_rope():
+    inp = workloads.small_decode(15, 2, 16, [900, 300], page_size=16, rec=368, outer=0.8, max_splits=3,
+                                 topk=200, invalid_frac=0.2)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, [0, 1])
+    compare(out, lse, ref_out, ref_lse, [0, 1], "sparse15")
 
 
 def test_sparse_all_masked_and_masked_pages():
