@@ -40,7 +40,12 @@ constexpr int kBN = 64;                 // key tile (the P-quantization schedule
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // 256 query rows per workgroup
-constexpr int kPitch = 208;             // bf16 elements per LDS row (416 B): conflict-free
+// LDS row pitches (bf16 elements), chosen so the operand reads hit distinct
+// banks: K fragments are 16-byte reads of 32 rows per half-wavefront (pitch
+// 100 dwords, 4 x odd); V^T fragments are 8-byte transposing reads of 8 rows
+// x 16 dwords per wavefront (pitch 80 dwords, 16 x odd).
+constexpr int kPitchK = 200;
+constexpr int kPitchV = 160;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -148,21 +153,20 @@ struct AttnParams {
 };
 
 struct AttnSmem {
-    uint16_t kt[2][kBN * kPitch];   // 2 x 26624 B
-    uint16_t vt[2][kBN * kPitch];   // 2 x 26624 B
+    uint16_t kt[2][kBN * kPitchK];  // 2 x 25600 B
+    uint16_t vt[2][kBN * kPitchV];  // 2 x 20480 B
     float pinv[256];                // P block scale code -> fp32(1 / fp32(e4m3(code) g_p)), 0 for d = 0
 };
 
-// e4m3 code of a P block with amax a >= 0: the quantizer's t = fp32(a / u)
-// by one multiply with fp32(1/u); the product lies within two ulps of the
-// quotient, so the code can differ only when it is within a few ulps of an
-// e4m3 rounding tie (or in the subnormal range, where the rounding is done
-// on t * 512): those lanes redo the exact division.
-__device__ __forceinline__ uint32_t p_scale_code(float a, float u, float inv_u) {
-    const float tq = a * inv_u;
+// The P block scale's t = fp32(a / u) is taken as one multiply with
+// fp32(1/u): the product lies within two ulps of the quotient, so its e4m3
+// code can differ only when it is within a few ulps of an e4m3 rounding tie
+// (mantissa bits below the kept 3 near one half) or in the subnormal range,
+// where the rounding is done on t * 512.  Such values redo the exact
+// division.
+__device__ __forceinline__ bool p_scale_near(float tq) {
     const uint32_t rem = f2u(tq) & 0xfffffu;
-    const bool near = tq < 0.015625f || (rem > 0x80000u - 8u && rem < 0x80000u + 8u);
-    return e4m3_encode(near ? a / u : tq);
+    return tq < 0.015625f || (rem > 0x80000u - 8u && rem < 0x80000u + 8u);
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -252,12 +256,12 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             const int c = tid + 512 * i;
-            *reinterpret_cast<u32x4*>(&sm.kt[buf][(c / 24) * kPitch + 8 * (c % 24)]) = sk[i];
+            *reinterpret_cast<u32x4*>(&sm.kt[buf][(c / 24) * kPitchK + 8 * (c % 24)]) = sk[i];
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 512 * i;
-            *reinterpret_cast<u32x4*>(&sm.vt[buf][(c >> 4) * kPitch + 8 * (c & 15)]) = sv[i];
+            *reinterpret_cast<u32x4*>(&sm.vt[buf][(c >> 4) * kPitchV + 8 * (c & 15)]) = sv[i];
         }
     };
 
@@ -273,13 +277,21 @@ void attn_kernel(AttnParams p) {
         const uint16_t* vb = sm.vt[buf];
         // ---- S^T for keys 32 mt2 .. +31
         f32x16 s[2] = {f32x16{}, f32x16{}};
+        auto kfrag = [&](int kk, int mt2) {
+            return *reinterpret_cast<const u32x4*>(&kb[(32 * mt2 + l32) * kPitchK + 16 * kk + 8 * g2]);
+        };
+        // fragments one k-step ahead of their MFMAs
+        u32x4 af[2][2];
+        af[0][0] = kfrag(0, 0);
+        af[0][1] = kfrag(0, 1);
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) {
-#pragma unroll
-            for (int mt2 = 0; mt2 < 2; ++mt2) {
-                const u32x4 af = *reinterpret_cast<const u32x4*>(&kb[(32 * mt2 + l32) * kPitch + 16 * kk + 8 * g2]);
-                s[mt2] = mfma32_bf16(as_bf16x8(af), qf[kk], s[mt2]);
+            if (kk + 1 < 12) {
+                af[(kk + 1) & 1][0] = kfrag(kk + 1, 0);
+                af[(kk + 1) & 1][1] = kfrag(kk + 1, 1);
             }
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2) s[mt2] = mfma32_bf16(as_bf16x8(af[kk & 1][mt2]), qf[kk], s[mt2]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- softmax: z in log2 units; the running max refreshed per tile
@@ -319,21 +331,41 @@ void attn_kernel(AttnParams p) {
         // ---- P operands per 16-key block kb
         f16x8 pf[4];
         bf16x8 ph[4], pm[4], pl[4];
+        if constexpr (kQuantP) {
+            // block amax, then the four blocks' scales side by side (the rare
+            // exact divisions in one uniform branch)
+            float am[4], tq[4];
+            bool nr[4];
+            bool any_near = false;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            float x[8];
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x16& t = s[kb >> 1];
+                const int o8 = 8 * (kb & 1);
+                am[kb] = fmaxf(fmaxf(fmaxf(t[o8], t[o8 + 1]), fmaxf(t[o8 + 2], t[o8 + 3])),
+                               fmaxf(fmaxf(t[o8 + 4], t[o8 + 5]), fmaxf(t[o8 + 6], t[o8 + 7])));
+            }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = s[kb >> 1][8 * (kb & 1) + i];
-            if constexpr (kQuantP) {
-                float am = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-                am = xor32_max(am);
-                const uint32_t code = p_scale_code(am, p.u_p, p.inv_u_p);
+            for (int kb = 0; kb < 4; ++kb) {
+                am[kb] = xor32_max(am[kb]);
+                tq[kb] = am[kb] * p.inv_u_p;
+                nr[kb] = p_scale_near(tq[kb]);
+                any_near |= nr[kb];
+            }
+            if (__any(any_near)) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) tq[kb] = nr[kb] ? am[kb] / p.u_p : tq[kb];
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x16& t = s[kb >> 1];
+                const int o8 = 8 * (kb & 1);
+                const uint32_t code = e4m3_encode(tq[kb]);
                 const float inv = sm.pinv[code];
                 const float sval = e4m3_decode(code);
-                uint32_t c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0] * inv, x[1] * inv, 1.0f, 0);
-                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[2] * inv, x[3] * inv, 1.0f, 1);
-                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[4] * inv, x[5] * inv, 1.0f, 2);
-                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, x[6] * inv, x[7] * inv, 1.0f, 3);
+                uint32_t c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[o8] * inv, t[o8 + 1] * inv, 1.0f, 0);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, t[o8 + 2] * inv, t[o8 + 3] * inv, 1.0f, 1);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, t[o8 + 4] * inv, t[o8 + 5] * inv, 1.0f, 2);
+                c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c8, t[o8 + 6] * inv, t[o8 + 7] * inv, 1.0f, 3);
                 if constexpr (kF16) {
                     const _Float16 sh = (_Float16)sval;
                     const f16x2 ss = {sh, sh};
@@ -352,12 +384,17 @@ void attn_kernel(AttnParams p) {
                                              pack_bf16_exact(d2[0] * sval, d2[1] * sval),
                                              pack_bf16_exact(d3[0] * sval, d3[1] * sval)});
                 }
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
                 // three bf16 parts (|p - hi - mid - lo| <= 2^-24 |p|)
+                const f32x16& t = s[kb >> 1];
+                const int o8 = 8 * (kb & 1);
                 u32x4 hv, mv, lv;
 #pragma unroll
                 for (int pr = 0; pr < 4; ++pr) {
-                    const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+                    const float x0 = t[o8 + 2 * pr], x1 = t[o8 + 2 * pr + 1];
                     const uint32_t h1 = pack_bf16_rne(x0, x1);
                     const float e0 = x0 - bf16_lo(h1), e1 = x1 - bf16_hi(h1);
                     const uint32_t m1 = pack_bf16_rne(e0, e1);
@@ -376,18 +413,29 @@ void attn_kernel(AttnParams p) {
         // 16-lane group lane s addresses key row k0 + s/4 and dims c0 + 4(s%4)
         // .. +3, and receives the 4 keys of dim c0 + s.
         const int s16 = lane & 15;
-        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitch + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+        auto vfrag = [&](int kb, int dt) {
+            const uint16_t* a0 = vbase + 16 * kb * kPitchV + 32 * dt;
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
+            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitchV)));
+            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
+            return u32x4{y1[0], y1[1], y2[0], y2[1]};
+        };
+        // the fragments of k-step kb + 1 are read during k-step kb's products
+        u32x4 vf[2][4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(0, dt);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            if (kb + 1 < 4) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(kb + 1, dt);
+            }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const uint16_t* a0 = vbase + 16 * kb * kPitch + 32 * dt;
-                const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
-                const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitch)));
-                const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-                const u32x4 va = u32x4{y1[0], y1[1], y2[0], y2[1]};
+                const u32x4 va = vf[kb & 1][dt];
                 if constexpr (kF16) {
                     o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, va), pf[kb], o[dt]);
                 } else {
