@@ -4,12 +4,13 @@
 Step (timed unit): one decode serving step of the dense workload B=64
 sequences x 128 heads x 4096 cached tokens (pages of 64, 432-byte records,
 4 splits + merge): the NVFP4 cache write of the batch's 64 new tokens
-followed by the paged split-K decode (one kernel, merge fused).  Inputs are
+followed by one paged split-K decode call (decode kernel + split merge
+kernel).  Inputs are
 resident in HBM before timing starts; the cache is rotated over 4 copies
 (> 256 MB Infinity Cache) so that decode reads come from HBM.
 
 Printed: one JSON line with queries/s (B / step time), the roofline of the
-decode kernel (HIP events around every timed launch, on the launch stream),
+decode call (HIP events around every timed call, on the launch stream),
 the oracle's CPU throughput on a bounded sample, and extra lines for the
 other paths (16-head decode, top-k sparse decode, prefill).
 
@@ -134,9 +135,10 @@ DECODE_SOURCES = ("decode.hip", "device_common.hpp", "launch.hpp")
 
 
 def measured_traffic():
-    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
-    counter summary, or None when the decode kernel's sources have changed
-    since those counters were taken (the summary records their sha256)."""
+    """HBM bytes per decode call (decode and split-merge kernels) from the
+    committed FETCH_SIZE/WRITE_SIZE counter summary, or None when the decode
+    kernels' sources have changed since those counters were taken (the
+    summary records their sha256)."""
     import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
@@ -282,11 +284,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "dense NVFP4 MLA decode step: B=64, H=128, L=4096, page 64, 432-byte records, "
-                               "4 splits + fused merge, plus NVFP4 cache write of 64 new tokens",
+                               "4 splits + merge kernel, plus NVFP4 cache write of 64 new tokens",
                    "global_batch": B, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-                     "kernel": "decode_kernel", "kernel_us": k_ms * 1e3,
+                     "kernel": "decode_kernel + split_merge_kernel (one decode call)", "kernel_us": k_ms * 1e3,
                      "flops_per_launch": flops, "bytes_per_launch": nbytes},
         "hbm": {"achieved_gbps": gbps, "peak_gbps": PEAK_HBM_GBPS, "frac": gbps / PEAK_HBM_GBPS},
     }
