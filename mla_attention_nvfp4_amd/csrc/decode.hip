@@ -316,14 +316,22 @@ void decode_kernel(DecodeArgs p) {
         };
         // two column tiles per step (the hi and lo MFMAs of one accumulator
         // are separated by the other tile's)
+        // fragments one step ahead of their products
+        bf16x8 va = vt_frag(0), vb = vt_frag(1);
 #pragma unroll
         for (int c = 0; c < 32; c += 2) {
-            const bf16x8 va = vt_frag(c), vb = vt_frag(c + 1);
+            bf16x8 na = va, nb = vb;
+            if (c + 2 < 32) {
+                na = vt_frag(c + 2);
+                nb = vt_frag(c + 3);
+            }
             o[c] = mfma16x16x32(va, ph, o[c]);
             o[c + 1] = mfma16x16x32(vb, ph, o[c + 1]);
             o[c] = mfma16x16x32(va, pl, o[c]);
             o[c + 1] = mfma16x16x32(vb, pl, o[c + 1]);
             __builtin_amdgcn_sched_barrier(0);
+            va = na;
+            vb = nb;
         }
     };
 
