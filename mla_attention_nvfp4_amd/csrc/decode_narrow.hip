@@ -9,10 +9,10 @@
 // the per-layer outer scale on read; review 2: Q is not quantized.
 //
 // Work item: workgroup (split s, sequence b) of 4 wavefronts; wavefront w
-// takes the split's 16-token tiles w, w+4, ...  Per tile, software-
-// pipelined: page-table walk three tiles ahead, record loads two tiles ahead
-// into registers, then
-//   S^T = K Q^T (16 tokens x 16 heads).  Lane l covers token l%16 and the
+// takes the split's 32-token tiles w, w+4, ... (two 16-token halves whose
+// chains interleave).  Per tile, software-pipelined: page-table walk two
+// tiles ahead, record loads one tile ahead into registers, then
+//   S^T = K Q^T (per half: 16 tokens x 16 heads).  Lane l covers token l%16 of each half and the
 //     latent dims 128(l/16) .. +127 (k-step kk: dims 128(l/16) + 8kk .. +7;
 //     the k-slot order is a permutation shared by both operands), so each
 //     lane dequantizes the 64 code bytes and 8 scales of its own token
@@ -24,9 +24,9 @@
 //     arbitrary bf16 RoPE values need not fit fp16's range.
 //   online softmax in base 2 with lazy rescaling; P as fp16 hi + lo
 //     (|p - hi - lo| <= 2^-22 |p|);
-//   O^T = V^T P^T with v_mfma_f32_16x16x16_f16: the dequantized latent
-//     goes to this wavefront's own LDS tile (token-major) and V^T is read
-//     back by ds_read_b64_tr_b16.
+//   O^T = V^T P^T with v_mfma_f32_16x16x32_f16 (k = the tile's 32 tokens):
+//     the dequantized latent goes to this wavefront's own LDS tile
+//     (token-major) and V^T is read back by ds_read_b64_tr_b16.
 // The four wavefronts then merge their (O, m, l) in LDS; single-split
 // sequences are written out, split ones go to the workspace for
 // split_merge_kernel.
@@ -44,14 +44,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kNW = 4;            // wavefronts per workgroup
-constexpr int kNT = 16;           // tokens per wavefront tile
+constexpr int kNT = 32;           // tokens per wavefront tile (two 16-token halves)
 constexpr int kVP = 528;          // fp16 per V tile row (1056 B: conflict-free writes and transposed reads)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 
 struct NarrowSmem {
-    _Float16 vt[kNW][kNT * kVP];  // 4 x 16,896 B; reused for the output merge
+    _Float16 vt[kNW][kNT * kVP];  // 4 x 33,792 B; reused for the output merge
     float m[kNW][16], l[kNW][16];
 };
 
@@ -142,10 +142,10 @@ void decode_narrow_kernel(DecodeArgs p) {
     const float sc_lat = sc_rope * outer * q_unscale;
 
     // ---- token addressing: tile j of this wavefront covers items
-    // i0 + kNT*(w + kNW*j) .. +15; lane l handles item + c16.
-    auto item_of = [&](int j) { return i0 + kNT * (w + kNW * j) + c16; };
-    auto position_of = [&](int j) -> int {
-        const int item = item_of(j);
+    // i0 + kNT*(w + kNW*j) .. +31; lane l handles item + 16 h2 + c16 of half h2.
+    auto item_of = [&](int j, int h2) { return i0 + kNT * (w + kNW * j) + 16 * h2 + c16; };
+    auto position_of = [&](int j, int h2) -> int {
+        const int item = item_of(j, h2);
         const int ic = min(item, max(n_items - 1, 0));
         const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
         return (j < nmine && item < i1 && pos >= 0 && pos < L) ? pos : -1;
@@ -179,54 +179,75 @@ void decode_narrow_kernel(DecodeArgs p) {
     float m_run = -INFINITY, l_run = 0.0f;
     _Float16* vt = sm.vt[w];
 
-    auto compute = [&](const Staged& st, int64_t off) {
-        const bool valid = off >= 0;
-        // validity of tokens 0..15 of the tile (lane c16 of group 0 has token c16)
-        const uint32_t vm = (uint32_t)__ballot(valid && gq == 0) & 0xffffu;
-        // ---- S^T: RoPE k-steps (bf16), then the latent ones (fp16)
-        // (latent k-steps alternate between two accumulators)
-        f32x4 s_r = {0.f, 0.f, 0.f, 0.f}, s_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // one tile: halves h2 = 0, 1 (tokens 16 h2 .. +15 of the tile)
+    auto compute = [&](const Staged (&st)[2], const int64_t (&off)[2]) {
+        const bool valid0 = off[0] >= 0, valid1 = off[1] >= 0;
+        // validity of tokens 0..31 (lane c16 of group 0 holds token 16 h2 + c16)
+        const uint32_t vm = ((uint32_t)__ballot(valid0 && gq == 0) & 0xffffu) |
+                            (((uint32_t)__ballot(valid1 && gq == 0) & 0xffffu) << 16);
+        // ---- S^T of each half: RoPE k-steps (bf16), then the latent ones
+        // (fp16), the two halves' chains interleaved
+        f32x4 s_r[2], s_l[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            s_r[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s_l[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int kr = 0; kr < 2; ++kr) {
-            u32x4 a;
-            if (kRopeFp8) {
-                const uint32_t x0 = st.r[0][2 * kr], x1 = st.r[0][2 * kr + 1];
-                const u32x2 y0 = e4m3x4_to_bf16(x0), y1 = e4m3x4_to_bf16(x1);
-                a = u32x4{y0[0], y0[1], y1[0], y1[1]};
-            } else {
-                a = st.r[kr];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                u32x4 a;
+                if (kRopeFp8) {
+                    const uint32_t x0 = st[h2].r[0][2 * kr], x1 = st[h2].r[0][2 * kr + 1];
+                    const u32x2 y0 = e4m3x4_to_bf16(x0), y1 = e4m3x4_to_bf16(x1);
+                    a = u32x4{y0[0], y0[1], y1[0], y1[1]};
+                } else {
+                    a = st[h2].r[kr];
+                }
+                const u32x4 zero = {0u, 0u, 0u, 0u};
+                s_r[h2] = mfma16x16x32(as_bf16x8((h2 ? valid1 : valid0) ? a : zero), qr[kr], s_r[h2]);
             }
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            s_r = mfma16x16x32(as_bf16x8(valid ? a : zero), qr[kr], s_r);
         }
-        // the lane's 8 block scales (e4m3 -> fp32 by the hardware FP8
-        // conversion, exact); a masked token gets scale 0, hence zero K and V
-        const uint32_t sw0 = valid ? st.sc[0] : 0u, sw1 = valid ? st.sc[1] : 0u;
-        const f32x2 sf[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(sw0, false), __builtin_amdgcn_cvt_pk_f32_fp8(sw0, true),
-                             __builtin_amdgcn_cvt_pk_f32_fp8(sw1, false), __builtin_amdgcn_cvt_pk_f32_fp8(sw1, true)};
+        // the lane's 8 block scales per half (e4m3 -> fp32 by the hardware
+        // FP8 conversion, exact); a masked token gets scale 0, hence zero K, V
+        f32x2 sf[2][4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const bool v = h2 ? valid1 : valid0;
+            const uint32_t sw0 = v ? st[h2].sc[0] : 0u, sw1 = v ? st[h2].sc[1] : 0u;
+            sf[h2][0] = __builtin_amdgcn_cvt_pk_f32_fp8(sw0, false);
+            sf[h2][1] = __builtin_amdgcn_cvt_pk_f32_fp8(sw0, true);
+            sf[h2][2] = __builtin_amdgcn_cvt_pk_f32_fp8(sw1, false);
+            sf[h2][3] = __builtin_amdgcn_cvt_pk_f32_fp8(sw1, true);
+        }
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-            const uint32_t cw = st.c[kk >> 2][kk & 3];
-            const _Float16 sv = (_Float16)sf[kk >> 2][(kk >> 1) & 1];
-            const f16x2 ss = {sv, sv};
-            f16x8 a;
-            const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss;
-            const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss;
-            const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss;
-            const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss;
-            a[0] = v0[0]; a[1] = v0[1]; a[2] = v1[0]; a[3] = v1[1];
-            a[4] = v2[0]; a[5] = v2[1]; a[6] = v3[0]; a[7] = v3[1];
-            s_l[kk & 1] = mfma_k32_f16(a, qf[kk], s_l[kk & 1]);
-            *reinterpret_cast<f16x8*>(&vt[c16 * kVP + 128 * gq + 8 * kk]) = a;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const uint32_t cw = st[h2].c[kk >> 2][kk & 3];
+                const _Float16 sv = (_Float16)sf[h2][kk >> 2][(kk >> 1) & 1];
+                const f16x2 ss = {sv, sv};
+                const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ss;
+                const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ss;
+                const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ss;
+                const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss;
+                const f16x8 a = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+                s_l[h2] = mfma_k32_f16(a, qf[kk], s_l[h2]);
+                *reinterpret_cast<f16x8*>(&vt[(16 * h2 + c16) * kVP + 128 * gq + 8 * kk]) = a;
+            }
         }
-        // ---- online softmax: element i is token 4gq + i of head c16
-        float z[4];
+        // ---- online softmax: z[h2][i] is token 16 h2 + 4gq + i of head c16
+        float z[2][4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = ((vm >> (4 * gq + i)) & 1u) ? sc_lat * (s_l[0][i] + s_l[1][i]) + sc_rope * s_r[i] : -INFINITY;
-            mx = fmaxf(mx, z[i]);
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[h2][i] = ((vm >> (16 * h2 + 4 * gq + i)) & 1u) ? sc_lat * s_l[h2][i] + sc_rope * s_r[h2][i]
+                                                                 : -INFINITY;
+                mx = fmaxf(mx, z[h2][i]);
+            }
         mx = xor32_max(xor16_max(mx));
         const bool move = mx > m_run + kRescaleSlack;
         const float m_new = move ? mx : m_run;
@@ -234,10 +255,12 @@ void decode_narrow_kernel(DecodeArgs p) {
         const float alpha = (move && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         float psum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = live ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.0f;
-            psum += z[i];
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[h2][i] = live ? __builtin_amdgcn_exp2f(z[h2][i] - m_new) : 0.0f;
+                psum += z[h2][i];
+            }
         psum = xor32_sum(xor16_sum(psum));
         l_run = alpha * l_run + psum;
         m_run = m_new;
@@ -245,62 +268,85 @@ void decode_narrow_kernel(DecodeArgs p) {
 #pragma unroll
             for (int c = 0; c < 32; ++c) o[c] *= alpha;
         }
-        // P as fp16 hi + lo; B operand: head c16, k-slots = tokens 4gq .. +3
-        f16x4 ph, pl;
+        // P as fp16 hi + lo; B operand of O^T = V^T P^T (k = 32 tokens): slot
+        // j < 4 is token 4gq + j, slot j >= 4 is token 16 + 4gq + j - 4
+        f16x8 ph, pl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ph[i] = (_Float16)z[i];
-            pl[i] = (_Float16)(z[i] - (float)ph[i]);
-        }
-        // ---- O^T = V^T P^T: A fragment of dim tile c by a transposing read;
-        // in each 16-lane group lane s addresses token 4gq + s/4, dims
-        // 16c + 4(s%4) .. +3, and receives the 4 tokens of dim 16c + s.
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ph[4 * h2 + i] = (_Float16)z[h2][i];
+                pl[4 * h2 + i] = (_Float16)(z[h2][i] - (float)ph[4 * h2 + i]);
+            }
+        // ---- O^T = V^T P^T on v_mfma_f32_16x16x32_f16: A fragment of dim
+        // tile c by two transposing reads (tokens 4gq .. +3 and 16 + 4gq ..
+        // +3); in each 16-lane group lane s addresses token row k0 + s/4 and
+        // dims 16c + 4(s%4) .. +3, and receives the 4 tokens of dim 16c + s.
         const _Float16* vb = vt + (4 * gq + (c16 >> 2)) * kVP + 4 * (c16 & 3);
         auto vfrag = [&](int c) {
-            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
                 const_cast<__attribute__((address_space(3))) _Float16*>(
                     (__attribute__((address_space(3))) const _Float16*)(vb + 16 * c))));
-            return __builtin_bit_cast(f16x4, x);
+            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+                const_cast<__attribute__((address_space(3))) _Float16*>(
+                    (__attribute__((address_space(3))) const _Float16*)(vb + 16 * kVP + 16 * c))));
+            const f16x4 y1 = __builtin_bit_cast(f16x4, x1), y2 = __builtin_bit_cast(f16x4, x2);
+            return f16x8{y1[0], y1[1], y1[2], y1[3], y2[0], y2[1], y2[2], y2[3]};
         };
-        // all 32 fragments first (one LDS round trip), then the products
-        f16x4 vf[32];
+        // fragments in groups of 8 dim tiles, the next group read during
+        // this group's products
+        f16x8 vf[2][8];
 #pragma unroll
-        for (int c = 0; c < 32; ++c) vf[c] = vfrag(c);
+        for (int c = 0; c < 8; ++c) vf[0][c] = vfrag(c);
 #pragma unroll
-        for (int c = 0; c < 32; c += 2) {
-            o[c] = mfma_k16_f16(vf[c], ph, o[c]);
-            o[c + 1] = mfma_k16_f16(vf[c + 1], ph, o[c + 1]);
-            o[c] = mfma_k16_f16(vf[c], pl, o[c]);
-            o[c + 1] = mfma_k16_f16(vf[c + 1], pl, o[c + 1]);
+        for (int g = 0; g < 4; ++g) {
+            if (g + 1 < 4) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) vf[(g + 1) & 1][c] = vfrag(8 * (g + 1) + c);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) {
+                const int cc = 8 * g + c;
+                o[cc] = mfma_k32_f16(vf[g & 1][c], ph, o[cc]);
+                o[cc + 1] = mfma_k32_f16(vf[g & 1][c + 1], ph, o[cc + 1]);
+                o[cc] = mfma_k32_f16(vf[g & 1][c], pl, o[cc]);
+                o[cc + 1] = mfma_k32_f16(vf[g & 1][c + 1], pl, o[cc + 1]);
+            }
         }
     };
 
-    // ---- token loop: records of tiles j+1 and j+2 in flight, page-table
-    // entry of tile j+3 loading, index of tile j+4 loading (sparse)
+    // ---- token loop: records of tile j+1 in flight, page-table entries of
+    // tile j+2 loading, indices of tile j+3 loading (sparse)
     if (nmine > 0) {
-        Staged s0, s1, s2;
-        int64_t offA, offB, offC;
-        {
-            const int p0 = position_of(0), p1 = position_of(1), p2 = position_of(2);
-            offA = offset_of(p0, page_of(p0));
-            offB = offset_of(p1, page_of(p1));
-            offC = offset_of(p2, page_of(p2));
+        Staged cur[2], nxt[2];
+        int64_t offA[2], offB[2];
+        int posC[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int p0 = position_of(0, h2), p1 = position_of(1, h2);
+            offA[h2] = offset_of(p0, page_of(p0));
+            offB[h2] = offset_of(p1, page_of(p1));
+            posC[h2] = position_of(2, h2);
         }
-        load(s0, offA);
-        load(s1, offB);
-        int pos3 = position_of(3);
+        load(cur[0], offA[0]);
+        load(cur[1], offA[1]);
         for (int j = 0; j < nmine; ++j) {
-            const int pg3 = page_of(pos3);            // tile j+3, used at the end
-            const int pos4 = position_of(j + 4);
-            load(s2, offC);                            // tile j+2 (masked reloads past the end)
-            compute(s0, offA);
-            const int64_t offD = offset_of(pos3, pg3);
-            s0 = s1;
-            s1 = s2;
-            offA = offB;
-            offB = offC;
-            offC = offD;
-            pos3 = pos4;
+            int pgC[2], posD[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                pgC[h2] = page_of(posC[h2]);              // tile j+2, used at the end
+                posD[h2] = position_of(j + 3, h2);
+            }
+            load(nxt[0], offB[0]);                        // tile j+1 (masked reloads past the end)
+            load(nxt[1], offB[1]);
+            compute(cur, offA);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                cur[h2] = nxt[h2];
+                offA[h2] = offB[h2];
+                offB[h2] = offset_of(posC[h2], pgC[h2]);
+                posC[h2] = posD[h2];
+            }
         }
     }
 
