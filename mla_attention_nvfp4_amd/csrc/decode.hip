@@ -47,9 +47,28 @@ constexpr int kRing = 4;             // offset ring slots
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
+// PV precision.  P enters V^T P^T rounded to fp16 (relative error <= 2^-11),
+// so the output moves by at most 2^-11 max|V| from that rounding; a tile
+// whose dequantized latent may exceed kSinglePBound in magnitude (outer x 6 x
+// block scale) adds a second product with the residual p - fp16(p), which
+// makes P exact to about 2^-22 relative.  With the bound at 8 the single-pass
+// error stays below 4e-3 absolute.
+constexpr float kSinglePBound = 8.0f;
+
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_f32_16x16x32_f16, same lane layout as the bf16 form
+__device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // Q k-steps kept in LDS (B-operand layout, 16 B per lane) instead of
 // registers: the RoPE part and the first kQLdsLatent latent k-steps.
@@ -62,6 +81,7 @@ struct DecodeSmem {
     u32x4 qs[NW][kQLds][64];              // NW x 6 KB
     int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
     uint32_t valid[kRing];                // bit i: token i of the tile is unmasked
+    alignas(16) uint32_t wide[kRing][NW];  // wavefront w's records of the tile exceed the single-pass bound
 };
 
 
@@ -72,6 +92,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 void decode_kernel(DecodeArgs p) {
     constexpr int kRec = kRopeFp8 ? 368 : 432;
     constexpr int kRpw = kTile / NW;                         // records per wavefront
+    static_assert(NW == 8, "the per-tile flags are read as two 4-word vectors");
     __shared__ DecodeSmem<NW> sm;
 
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
@@ -93,19 +114,42 @@ void decode_kernel(DecodeArgs p) {
     const int hq = h_base + c16;
 
     // Q as the B operand of S^T = K Q^T: k-step kk covers d = 32kk..32kk+31
-    // (kk 16, 17: RoPE).  Latent k-steps kQLdsLatent..15 stay in registers
-    // (qf[kk - kQLdsLatent]); the others go to this wavefront's LDS slots
-    // (slot kk for kk < kQLdsLatent, kQLdsLatent + kk - 16 for RoPE).
-    bf16x8 qf[16 - kQLdsLatent];
+    // (kk 16, 17: RoPE).  Latent k-steps are fp16, scaled by 2^(14 - E)
+    // where 2^E <= max |q_nope| of the head < 2^(E+1) (bf16 -> fp16 exact
+    // down to 2^-24 of the head's largest value); RoPE k-steps stay bf16.
+    // Latent k-steps kQLdsLatent..15 stay in registers (qf[kk -
+    // kQLdsLatent]); the others go to this wavefront's LDS slots (slot kk
+    // for kk < kQLdsLatent, kQLdsLatent + kk - 16 for RoPE).
+    f16x8 qf[16 - kQLdsLatent];
+    float q_unscale;   // 2^(E - 14)
     {
         const bool ok = hq < p.H;
         const u32x4 zero = {0u, 0u, 0u, 0u};
         const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(ok ? hq : 0) * p.q_stride_h + 8 * gq;
+        u32x4 raw[16];
+        float amax = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-            const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero;
-            if (kk < kQLdsLatent) sm.qs[w][kk][lane] = v;
-            else qf[kk - kQLdsLatent] = as_bf16x8(v);
+            raw[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(raw[kk][j])), __builtin_fabsf(bf16_hi(raw[kk][j]))));
+        }
+        amax = xor32_max(xor16_max(amax));   // over the head's four lanes c16 + 16gq
+        int E = amax > 0.0f ? (int)((f2u(amax) >> 23) & 0xffu) - 127 : 0;
+        E = E < -100 ? -100 : E;
+        const int sh = 14 - E;
+        q_unscale = __builtin_ldexpf(1.0f, E - 14);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            f16x8 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(raw[kk][j]), sh);
+                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(raw[kk][j]), sh);
+            }
+            if (kk < kQLdsLatent) sm.qs[w][kk][lane] = __builtin_bit_cast(u32x4, v);
+            else qf[kk - kQLdsLatent] = v;
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -114,8 +158,9 @@ void decode_kernel(DecodeArgs p) {
 
     const uint8_t* __restrict__ cache = p.cache;
     const float outer = p.outer_scale;
-    const float inv_outer = 1.0f / outer;
-    const float score_scale = p.softmax_scale * kLog2e * outer;
+    const float lat_scale = outer * q_unscale;            // latent partial sum -> outer * q.k
+    const float score_scale = p.softmax_scale * kLog2e;   // log2 units
+    const float wide_scale = kSinglePBound / (6.0f * outer);   // block scales above this need the residual pass
 
     // ---- offsets.  Loads are issued by every lane of wavefront 0 from
     // clamped (always valid) addresses and masked afterwards, so the
@@ -177,18 +222,26 @@ void decode_kernel(DecodeArgs p) {
     auto dequant = [&](int kbuf, int slot) {
         uint16_t* ks = sm.ks[kbuf];
         const uint32_t vmask = sm.valid[slot];
+        bool big = false;
 #pragma unroll
         for (int r = 0; r < kRpw; ++r) {
             const int tok = kRpw * w + r;
             const bool valid = (vmask >> tok) & 1u;
-            const uint32_t c = valid ? rc[r] : 0u;
-            const float sc = e4m3_hw<0>(valid ? rs[r] : 0u);
-            const f32x2 v0 = e2m1_pair<0>(c), v1 = e2m1_pair<1>(c);
-            const f32x2 v2 = e2m1_pair<2>(c), v3 = e2m1_pair<3>(c);
-            const u32x4 wv = {pack_bf16_exact(v0[0] * sc, v0[1] * sc), pack_bf16_exact(v1[0] * sc, v1[1] * sc),
-                              pack_bf16_exact(v2[0] * sc, v2[1] * sc), pack_bf16_exact(v3[0] * sc, v3[1] * sc)};
-            *reinterpret_cast<u32x4*>(&ks[tok * kKsPitch + 8 * lane]) = wv;
+            // masked: scale 0 (the code word of record 0 is finite)
+            const float scf = e4m3_hw<0>(valid ? rs[r] : 0u);
+            big = big || scf > wide_scale;
+            const _Float16 sc = (_Float16)scf;
+            const f16x2 ss = {sc, sc};
+            const uint32_t c = rc[r];
+            const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * ss;
+            const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * ss;
+            const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * ss;
+            const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * ss;
+            const f16x8 wv = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+            *reinterpret_cast<f16x8*>(&ks[tok * kKsPitch + 8 * lane]) = wv;
         }
+        const bool wbig = __any(big);
+        if (lane == 0) sm.wide[slot][w] = wbig ? 1u : 0u;
         // RoPE: kRpw tokens x 8 units of 8 elements
         if (lane < 8 * kRpw) {
             const int tok = kRpw * w + (lane >> 3), u = lane & 7;
@@ -217,38 +270,41 @@ void decode_kernel(DecodeArgs p) {
     auto compute = [&](int kbuf, int slot) {
         const uint16_t* ks = sm.ks[kbuf];
         // S^T accumulators, one per 16-token half of the tile (consecutive
-        // MFMAs alternate between them): the RoPE k-steps go first, the
-        // accumulators are then divided by the outer scale, and the latent
-        // k-steps follow, so that outer * S restores the scale on the latent
-        // part only.
+        // MFMAs alternate between them): the latent k-steps (fp16) go first,
+        // the accumulators are then multiplied by outer * 2^(E - 14), and
+        // the RoPE k-steps (bf16) follow.
         f32x4 sa[2];
         sa[0] = sa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto ks_frag = [&](int kk, int tt) {
             return *reinterpret_cast<const u32x4*>(&ks[(16 * tt + c16) * kKsPitch + 32 * kk + 8 * gq]);
         };
-        auto order = [](int i) { return i < 2 ? 16 + i : i - 2; };
         auto q_lds = [](int kk) { return kk < kQLdsLatent || kk >= 16; };
         auto q_slot = [](int kk) { return kk < kQLdsLatent ? kk : kQLdsLatent + kk - 16; };
         // fragments (and LDS-held Q) one k-step ahead of their MFMAs
         u32x4 f0[2], f1[2], qb[2];
-        f0[0] = ks_frag(order(0), 0);
-        f1[0] = ks_frag(order(0), 1);
-        qb[0] = sm.qs[w][q_slot(order(0))][lane];
+        f0[0] = ks_frag(0, 0);
+        f1[0] = ks_frag(0, 1);
+        qb[0] = sm.qs[w][q_slot(0)][lane];
 #pragma unroll
-        for (int i = 0; i < 18; ++i) {
-            if (i + 1 < 18) {
-                f0[(i + 1) & 1] = ks_frag(order(i + 1), 0);
-                f1[(i + 1) & 1] = ks_frag(order(i + 1), 1);
-                if (q_lds(order(i + 1))) qb[(i + 1) & 1] = sm.qs[w][q_slot(order(i + 1))][lane];
+        for (int kk = 0; kk < 18; ++kk) {
+            if (kk + 1 < 18) {
+                f0[(kk + 1) & 1] = ks_frag(kk + 1, 0);
+                f1[(kk + 1) & 1] = ks_frag(kk + 1, 1);
+                if (q_lds(kk + 1)) qb[(kk + 1) & 1] = sm.qs[w][q_slot(kk + 1)][lane];
             }
-            if (i == 2) {
-                sa[0] *= inv_outer;
-                sa[1] *= inv_outer;
+            if (kk < 16) {
+                const f16x8 qv = q_lds(kk) ? __builtin_bit_cast(f16x8, qb[kk & 1]) : qf[kk - kQLdsLatent];
+                sa[0] = mfma_k32_f16(__builtin_bit_cast(f16x8, f0[kk & 1]), qv, sa[0]);
+                sa[1] = mfma_k32_f16(__builtin_bit_cast(f16x8, f1[kk & 1]), qv, sa[1]);
+            } else {
+                if (kk == 16) {
+                    sa[0] *= lat_scale;
+                    sa[1] *= lat_scale;
+                }
+                const bf16x8 qv = as_bf16x8(qb[kk & 1]);
+                sa[0] = mfma16x16x32(as_bf16x8(f0[kk & 1]), qv, sa[0]);
+                sa[1] = mfma16x16x32(as_bf16x8(f1[kk & 1]), qv, sa[1]);
             }
-            const int kk = order(i);
-            const bf16x8 qv = q_lds(kk) ? as_bf16x8(qb[i & 1]) : qf[kk - kQLdsLatent];
-            sa[0] = mfma16x16x32(as_bf16x8(f0[i & 1]), qv, sa[0]);
-            sa[1] = mfma16x16x32(as_bf16x8(f1[i & 1]), qv, sa[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
@@ -287,19 +343,14 @@ void decode_kernel(DecodeArgs p) {
 #pragma unroll
             for (int c = 0; c < 32; ++c) o[c] *= alpha;
         }
-        // P as bf16 hi + lo (|p - hi - lo| <= 2^-16 |p|): one bf16 rounding
-        // of P alone can exceed the output tolerance when V has large
-        // outliers.  k-slot j < 4 is token 4gq + j, j >= 4 is token
-        // 16 + 4gq + j - 4 (the same slots as the V^T fragment below).
-        u32x4 h, lo;
+        // P as fp16 (B operand): k-slot j < 4 is token 4gq + j, j >= 4 is
+        // token 16 + 4gq + j - 4 (the same slots as the V^T fragment below);
+        // the residual p - fp16(p) is formed only for a tile that needs it.
+        f16x8 ph;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            h[2 * tt] = pack_bf16_rne(pv[tt][0], pv[tt][1]);
-            h[2 * tt + 1] = pack_bf16_rne(pv[tt][2], pv[tt][3]);
-            lo[2 * tt] = pack_bf16_rne(pv[tt][0] - bf16_lo(h[2 * tt]), pv[tt][1] - bf16_hi(h[2 * tt]));
-            lo[2 * tt + 1] = pack_bf16_rne(pv[tt][2] - bf16_lo(h[2 * tt + 1]), pv[tt][3] - bf16_hi(h[2 * tt + 1]));
-        }
-        const bf16x8 ph = as_bf16x8(h), pl = as_bf16x8(lo);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ph[4 * tt + i] = (_Float16)pv[tt][i];
         // V^T fragment of column tile c by transposing reads: within each
         // 16-lane group, lane s addresses token 4gq + s/4 (+16 for the
         // second half) and columns 16c + 4(s%4) .. +3; lane i receives the 4
@@ -312,27 +363,37 @@ void decode_kernel(DecodeArgs p) {
             const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(vb1 + 4 * c));
             const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(vb2 + 4 * c));
             const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-            return as_bf16x8(u32x4{y1[0], y1[1], y2[0], y2[1]});
+            return __builtin_bit_cast(f16x8, u32x4{y1[0], y1[1], y2[0], y2[1]});
         };
-        // two column tiles per step (the hi and lo MFMAs of one accumulator
-        // are separated by the other tile's)
-        // fragments one step ahead of their products
-        bf16x8 va = vt_frag(0), vb = vt_frag(1);
+        // two column tiles per step, fragments one step ahead of their
+        // products; the residual pass (rare) is a second sweep
+        auto pv_sweep = [&](const f16x8& pp) {
+            f16x8 va = vt_frag(0), vb = vt_frag(1);
 #pragma unroll
-        for (int c = 0; c < 32; c += 2) {
-            bf16x8 na = va, nb = vb;
-            if (c + 2 < 32) {
-                na = vt_frag(c + 2);
-                nb = vt_frag(c + 3);
+            for (int c = 0; c < 32; c += 2) {
+                f16x8 na = va, nb = vb;
+                if (c + 2 < 32) {
+                    na = vt_frag(c + 2);
+                    nb = vt_frag(c + 3);
+                }
+                o[c] = mfma_k32_f16(va, pp, o[c]);
+                o[c + 1] = mfma_k32_f16(vb, pp, o[c + 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                va = na;
+                vb = nb;
             }
-            o[c] = mfma16x16x32(va, ph, o[c]);
-            o[c + 1] = mfma16x16x32(vb, ph, o[c + 1]);
-            o[c] = mfma16x16x32(va, pl, o[c]);
-            o[c + 1] = mfma16x16x32(vb, pl, o[c + 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            va = na;
-            vb = nb;
-        }
+        };
+        f16x8 pl;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pl[4 * tt + i] = (_Float16)(pv[tt][i] - (float)ph[4 * tt + i]);
+        pv_sweep(ph);
+        const u32x4 wa = *reinterpret_cast<const u32x4*>(&sm.wide[slot][0]);
+        const u32x4 wb = *reinterpret_cast<const u32x4*>(&sm.wide[slot][4]);
+        const u32x4 wo = wa | wb;
+        // (the flags are the same in every lane: a uniform branch)
+        if (__builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u) pv_sweep(pl);
     };
 
     if (T0 < T1) {
