@@ -49,6 +49,11 @@ constexpr int kVP = 528;          // fp16 per V tile row (1056 B: conflict-free 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
+// PV precision: P enters V^T P^T rounded to fp16 (relative error <= 2^-11,
+// so the output moves by at most 2^-11 max|V|); a tile whose dequantized
+// latent may exceed kSinglePBound in magnitude (outer x 6 x block scale)
+// adds a second sweep with the residual p - fp16(p).
+constexpr float kSinglePBound = 8.0f;
 
 struct NarrowSmem {
     _Float16 vt[kNW][kNT * kVP];  // 4 x 33,792 B; reused for the output merge
@@ -60,9 +65,6 @@ __device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
 }
 // D = A (16x16) * B (16x16) + C; lane l supplies row / column l % 16 with
 // k-slots 4*(l/16) .. +3 and receives D[4*(l/16) + i][l % 16].
-__device__ __forceinline__ f32x4 mfma_k16_f16(f16x4 a, f16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
 
 
 // The record bytes one lane needs for its token: 64 code bytes, 8 scale
@@ -140,6 +142,7 @@ void decode_narrow_kernel(DecodeArgs p) {
     const float outer = p.outer_scale;
     const float sc_rope = p.softmax_scale * kLog2e;
     const float sc_lat = sc_rope * outer * q_unscale;
+    const float wide_scale = kSinglePBound / (6.0f * outer);   // block scales above this need the residual sweep
 
     // ---- token addressing: tile j of this wavefront covers items
     // i0 + kNT*(w + kNW*j) .. +31; lane l handles item + 16 h2 + c16 of half h2.
@@ -212,6 +215,7 @@ void decode_narrow_kernel(DecodeArgs p) {
         // the lane's 8 block scales per half (e4m3 -> fp32 by the hardware
         // FP8 conversion, exact); a masked token gets scale 0, hence zero K, V
         f32x2 sf[2][4];
+        bool big = false;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const bool v = h2 ? valid1 : valid0;
@@ -220,7 +224,10 @@ void decode_narrow_kernel(DecodeArgs p) {
             sf[h2][1] = __builtin_amdgcn_cvt_pk_f32_fp8(sw0, true);
             sf[h2][2] = __builtin_amdgcn_cvt_pk_f32_fp8(sw1, false);
             sf[h2][3] = __builtin_amdgcn_cvt_pk_f32_fp8(sw1, true);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) big = big || fmaxf(sf[h2][k][0], sf[h2][k][1]) > wide_scale;
         }
+        const bool residual = __any(big);   // uniform: the wavefront's tile needs the second sweep
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
 #pragma unroll
@@ -268,8 +275,9 @@ void decode_narrow_kernel(DecodeArgs p) {
 #pragma unroll
             for (int c = 0; c < 32; ++c) o[c] *= alpha;
         }
-        // P as fp16 hi + lo; B operand of O^T = V^T P^T (k = 32 tokens): slot
-        // j < 4 is token 4gq + j, slot j >= 4 is token 16 + 4gq + j - 4
+        // P as fp16 hi (+ lo = the residual); B operand of O^T = V^T P^T (k =
+        // 32 tokens): slot j < 4 is token 4gq + j, slot j >= 4 is token
+        // 16 + 4gq + j - 4
         f16x8 ph, pl;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -295,24 +303,22 @@ void decode_narrow_kernel(DecodeArgs p) {
         };
         // fragments in groups of 8 dim tiles, the next group read during
         // this group's products
-        f16x8 vf[2][8];
+        auto pv_sweep = [&](const f16x8& pp) {
+            f16x8 vf[2][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) vf[0][c] = vfrag(c);
+            for (int c = 0; c < 8; ++c) vf[0][c] = vfrag(c);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (g + 1 < 4) {
+            for (int g = 0; g < 4; ++g) {
+                if (g + 1 < 4) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) vf[(g + 1) & 1][c] = vfrag(8 * (g + 1) + c);
+                    for (int c = 0; c < 8; ++c) vf[(g + 1) & 1][c] = vfrag(8 * (g + 1) + c);
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) o[8 * g + c] = mfma_k32_f16(vf[g & 1][c], pp, o[8 * g + c]);
             }
-#pragma unroll
-            for (int c = 0; c < 8; c += 2) {
-                const int cc = 8 * g + c;
-                o[cc] = mfma_k32_f16(vf[g & 1][c], ph, o[cc]);
-                o[cc + 1] = mfma_k32_f16(vf[g & 1][c + 1], ph, o[cc + 1]);
-                o[cc] = mfma_k32_f16(vf[g & 1][c], pl, o[cc]);
-                o[cc + 1] = mfma_k32_f16(vf[g & 1][c + 1], pl, o[cc + 1]);
-            }
-        }
+        };
+        pv_sweep(ph);
+        if (residual) pv_sweep(pl);
     };
 
     // ---- token loop: records of tile j+1 in flight, page-table entries of

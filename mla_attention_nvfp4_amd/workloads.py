@@ -154,13 +154,16 @@ def decode_workload(n: int, H: int | None = None) -> DecodeInputs:
 def small_decode(seed: int, B: int, H: int, lens, page_size: int = 64, rec: int = 432,
                  outer: float = 1.0, softmax_scale: float | None = None, max_splits: int = 1,
                  shuffle: bool = True, outliers: bool = False, topk: int = 0,
-                 invalid_frac: float = 0.0) -> DecodeInputs:
-    """A small decode case for parity tests (same recipe as the workloads)."""
+                 invalid_frac: float = 0.0, kv_gain: float = 1.0) -> DecodeInputs:
+    """A small decode case for parity tests (same recipe as the workloads;
+    kv_gain multiplies the latent before it is rounded to bf16)."""
     g = torch.Generator().manual_seed(seed)
     q = _randn_bf16(g, (B, H, D_LATENT + D_ROPE), chunk_rows=max(1, B))
     pt, slots, offs, num_pages = _paged(g, lens, page_size, shuffle)
     T = int(offs[-1])
     kv_c = _randn_bf16(g, (max(T, 0), D_LATENT))
+    if kv_gain != 1.0:
+        kv_c = (kv_c.to(torch.float32) * kv_gain).to(torch.bfloat16)
     if outliers and T:
         hit = torch.rand((T, D_LATENT), generator=g) < 0.01
         kv_c[hit] = (kv_c[hit].to(torch.float32) * 20).to(torch.bfloat16)

@@ -36,6 +36,28 @@ def test_dense_small(case):
     compare(out, lse, ref_out, ref_lse, list(range(B)), f"dense{seed}")
 
 
+# Latent magnitudes around the single-pass bound of the PV product (|V| near
+# 8 at 1.9 sigma): tiles with and without the residual sweep in one
+# sequence, for the 128-head and the 16-head kernels.
+PV_BOUND = [
+    # seed, B, H, lens, page, rec, splits
+    (30, 2, 128, [1500, 700], 64, 432, 2),
+    (31, 2, 16, [1500, 700], 64, 368, 2),
+]
+
+
+@pytest.mark.parametrize("case", PV_BOUND, ids=[f"pvbound{c[0]}" for c in PV_BOUND])
+def test_dense_pv_bound(case):
+    seed, B, H, lens, page, rec, splits = case
+    inp = workloads.small_decode(seed, B, H, lens, page_size=page, rec=rec, max_splits=splits, kv_gain=1.9)
+    print(f"  pv-bound seed={seed} B={B} H={H} lens={lens} max|kv|={float(inp.kv_c.float().abs().max()):.2f}",
+          flush=True)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, list(range(B)))
+    compare(out, lse, ref_out, ref_lse, list(range(B)), f"pvbound{seed}")
+
+
 SMALL_SPARSE = [
     # seed, B, H, lens, topk, invalid_frac, splits
     (11, 3, 16, [100, 0, 700], 96, 0.1, 1),
@@ -93,7 +115,12 @@ def test_out_of_range_page_ids_are_masked():
                             torch.tensor([128], dtype=torch.int32, device="cuda"),
                             inp.outer_scale, inp.softmax_scale, 1)
     torch.cuda.synchronize()
-    assert torch.allclose(out, out2, rtol=1e-5, atol=1e-6) and torch.allclose(lse, lse2, atol=1e-5)
+    # The two launches cut the tokens into different tiles, so the running
+    # maximum, and with it the fp16 rounding of P, differs: the outputs agree
+    # to 2^-11 max|V| (single-pass bound), not bit for bit.
+    assert torch.isfinite(out).all()
+    assert float((out - out2).abs().max()) <= 2.0 ** -11 * 8.0
+    assert torch.allclose(lse, lse2, atol=1e-5)
 
 
 def test_split_counts_agree_and_runs_are_deterministic():
