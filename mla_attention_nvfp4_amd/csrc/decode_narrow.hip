@@ -241,7 +241,9 @@ void decode_narrow_kernel(DecodeArgs p) {
                 const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ss;
                 const f16x8 a = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
                 s_l[h2] = mfma_k32_f16(a, qf[kk], s_l[h2]);
-                *reinterpret_cast<f16x8*>(&vt[(16 * h2 + c16) * kVP + 128 * gq + 8 * kk]) = a;
+                // 16-byte chunk j of a tile row is stored at j ^ ((j >> 4) & 1):
+                // the 64 lanes of one store then cover every bank once
+                *reinterpret_cast<f16x8*>(&vt[(16 * h2 + c16) * kVP + 128 * gq + 8 * (kk ^ (gq & 1))]) = a;
             }
         }
         // ---- online softmax: z[h2][i] is token 16 h2 + 4gq + i of head c16
@@ -290,14 +292,16 @@ void decode_narrow_kernel(DecodeArgs p) {
         // tile c by two transposing reads (tokens 4gq .. +3 and 16 + 4gq ..
         // +3); in each 16-lane group lane s addresses token row k0 + s/4 and
         // dims 16c + 4(s%4) .. +3, and receives the 4 tokens of dim 16c + s.
-        const _Float16* vb = vt + (4 * gq + (c16 >> 2)) * kVP + 4 * (c16 & 3);
+        // (chunk 2c + (s%4)/2 sits at 2c + ((s%4)/2 ^ 1) in dim tiles c with bit 3 set)
+        const _Float16* vb0 = vt + (4 * gq + (c16 >> 2)) * kVP + 4 * (c16 & 3);
+        const _Float16* vb1 = vt + (4 * gq + (c16 >> 2)) * kVP + 8 * (((c16 & 3) >> 1) ^ 1) + 4 * (c16 & 1);
         auto vfrag = [&](int c) {
             const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
                 const_cast<__attribute__((address_space(3))) _Float16*>(
-                    (__attribute__((address_space(3))) const _Float16*)(vb + 16 * c))));
+                    (__attribute__((address_space(3))) const _Float16*)(((c >> 3) & 1 ? vb1 : vb0) + 16 * c))));
             const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
                 const_cast<__attribute__((address_space(3))) _Float16*>(
-                    (__attribute__((address_space(3))) const _Float16*)(vb + 16 * kVP + 16 * c))));
+                    (__attribute__((address_space(3))) const _Float16*)(((c >> 3) & 1 ? vb1 : vb0) + 16 * kVP + 16 * c))));
             const f16x4 y1 = __builtin_bit_cast(f16x4, x1), y2 = __builtin_bit_cast(f16x4, x2);
             return f16x8{y1[0], y1[1], y1[2], y1[3], y2[0], y2[1], y2[2], y2[3]};
         };
