@@ -79,7 +79,7 @@ template <int NW>
 struct DecodeSmem {
     uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
     u32x4 qs[NW][kQLds][64];              // NW x 6 KB
-    int64_t offs[kRing][kTile];           // record byte offset, -1 = masked
+    int64_t offs[kRing][kTile];           // record byte offset (masked tokens: 0, see valid)
     uint32_t valid[kRing];                // bit i: token i of the tile is unmasked
     alignas(16) uint32_t wide[kRing][NW];  // wavefront w's records of the tile exceed the single-pass bound
 };
@@ -181,7 +181,7 @@ void decode_kernel(DecodeArgs p) {
     };
     auto store_offs = [&](int slot, int64_t off) {
         const uint64_t vm = __ballot(lane < kTile && off >= 0);
-        if (lane < kTile) sm.offs[slot][lane] = off;
+        if (lane < kTile) sm.offs[slot][lane] = off < 0 ? 0 : off;   // masked: record 0, zeroed later
         if (lane == 0) sm.valid[slot] = (uint32_t)vm;
     };
     auto compute_offs = [&](int t, int slot) {
@@ -201,14 +201,12 @@ void decode_kernel(DecodeArgs p) {
     auto load_raw = [&](int slot) {
 #pragma unroll
         for (int r = 0; r < kRpw; ++r) {
-            const int64_t off = sm.offs[slot][kRpw * w + r];
-            const uint8_t* rp = cache + (off < 0 ? 0 : off);
+            const uint8_t* rp = cache + sm.offs[slot][kRpw * w + r];
             rc[r] = *reinterpret_cast<const uint32_t*>(rp + 4 * lane);
             rs[r] = rp[256 + (lane >> 1)];
         }
         const int r = (lane >> 3) % kRpw, u = lane & 7;
-        const int64_t off = sm.offs[slot][kRpw * w + r];
-        const uint8_t* rp = cache + (off < 0 ? 0 : off);
+        const uint8_t* rp = cache + sm.offs[slot][kRpw * w + r];
         if (kRopeFp8) {
             const u32x2 v2 = *reinterpret_cast<const u32x2*>(rp + 288 + 8 * u);
             rr = u32x4{v2[0], v2[1], 0u, 0u};
@@ -310,15 +308,22 @@ void decode_kernel(DecodeArgs p) {
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
         float z[2][4];
         float mx = -INFINITY;
-        const uint32_t vmask = sm.valid[slot];
+        const uint32_t vmask = __builtin_amdgcn_readfirstlane(sm.valid[slot]);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool valid = (vmask >> (16 * tt + 4 * gq + i)) & 1u;
-                z[tt][i] = valid ? score_scale * sa[tt][i] : -INFINITY;
-                mx = fmaxf(mx, z[tt][i]);
-            }
+            for (int i = 0; i < 4; ++i) z[tt][i] = score_scale * sa[tt][i];
+        if (vmask != 0xffffffffu) {   // (uniform) a tile with masked tokens
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((vmask >> (16 * tt + 4 * gq + i)) & 1u)) z[tt][i] = -INFINITY;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[tt][i]);
         mx = xor32_max(xor16_max(mx));
         // Lazy rescaling: the reference max moves only when a score exceeds
         // it by more than kRescaleSlack (log2 units), so p <= 2^8 and O is
@@ -383,17 +388,19 @@ void decode_kernel(DecodeArgs p) {
                 vb = nb;
             }
         };
-        f16x8 pl;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pl[4 * tt + i] = (_Float16)(pv[tt][i] - (float)ph[4 * tt + i]);
         pv_sweep(ph);
         const u32x4 wa = *reinterpret_cast<const u32x4*>(&sm.wide[slot][0]);
         const u32x4 wb = *reinterpret_cast<const u32x4*>(&sm.wide[slot][4]);
         const u32x4 wo = wa | wb;
         // (the flags are the same in every lane: a uniform branch)
-        if (__builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u) pv_sweep(pl);
+        if (__builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u) {
+            f16x8 pl;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pl[4 * tt + i] = (_Float16)(pv[tt][i] - (float)ph[4 * tt + i]);
+            pv_sweep(pl);
+        }
     };
 
     if (T0 < T1) {
