@@ -18,22 +18,23 @@
 //   staging   each wavefront loads its own 32/NW records of tile t+2 into
 //             registers (coalesced runs per record; no cross-wave traffic);
 //   dequant   each wavefront dequantizes its own records of tile t+1 into
-//             the free token-major tile (e2m1 code x e4m3 scale is exact in
-//             bf16; the outer scale is not folded), RoPE in columns
-//             512..575;
-//   compute   tile t: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = tile
-//             rows, B = the wavefront's Q rows in registers); the latent
-//             part of the accumulator is multiplied by the outer scale
-//             before the RoPE k-steps; online softmax in base 2 with lazy
-//             rescaling; P split into bf16 hi + lo parts (B operand) for
-//             O^T = V^T P^T, whose A operand is read from the same
-//             token-major tile with the transposing LDS load
-//             ds_read_b64_tr_b16 (V is the latent).
+//             the free token-major tile: latent as fp16 (e2m1 code x e4m3
+//             scale is exact in fp16; the outer scale is not folded), RoPE
+//             as bf16 in columns 512..575;
+//   compute   tile t: S^T = K Q^T on v_mfma_f32_16x16x32 (A = tile rows,
+//             B = the wavefront's Q; latent k-steps in fp16 with Q scaled
+//             by a power of two per head, then the accumulator scaled by
+//             outer * 2^(E-14), then the RoPE k-steps in bf16); online
+//             softmax in base 2 with lazy rescaling; P rounded to fp16 (B
+//             operand) for O^T = V^T P^T, whose A operand is read from the
+//             same token-major tile with the transposing LDS load
+//             ds_read_b64_tr_b16 (V is the latent); a tile whose latent may
+//             exceed the single-pass bound adds a sweep with the residual
+//             p - fp16(p).
 // The epilogue writes out = outer * O / l and lse = m + ln l (natural log)
 // to the output when the sequence has one split; otherwise it writes the
-// partial to the workspace and the last workgroup of the sequence and head
-// group to finish merges the partials in split order (same rule as
-// lse_merge_kernel), then resets the arrival counter.
+// partial to the workspace, and split_merge_kernel (launched after the
+// decode kernel) merges each sequence's partials in split order.
 #include "device_common.hpp"
 #include "launch.hpp"
 
