@@ -89,10 +89,11 @@ int mla_nvfp4_record_bytes(int rope_fp8);
 int mla_decode_num_splits(int seq_len, int max_splits);
 
 /* Bytes of decode workspace for B sequences, H heads, max_splits chunks:
- * partial outputs fp32 [B][max_splits][H][512], then partial LSE fp32
- * [B][max_splits][H], each region 256-byte aligned.  0 when
- * max_splits <= 1.  No initial contents are needed; calls that may run
- * concurrently need separate workspaces. */
+ * partial outputs [B][max_splits][H][512] (fp32 rows; a row may instead hold
+ * fp16 values in its first half), then partial LSE fp32 [B][max_splits][H],
+ * then one format byte per partial row [B][max_splits][H] (1 = fp16), each
+ * region 256-byte aligned.  0 when max_splits <= 1.  No initial contents are
+ * needed; calls that may run concurrently need separate workspaces. */
 size_t mla_decode_workspace_bytes(int B, int H, int max_splits);
 
 /* Bytes of a 128x4-swizzled e4m3 scale buffer for `rows` rows of

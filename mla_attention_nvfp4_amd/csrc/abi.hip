@@ -114,15 +114,19 @@ int check_decode(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_strid
 }
 
 size_t decode_ws_lse_bytes(int B, int H, int S) { return align256((size_t)B * S * H * sizeof(float)); }
+size_t decode_ws_fmt_bytes(int B, int H, int S) { return align256((size_t)B * S * H); }
 
 int run_decode(mla::DecodeArgs& a, void* workspace, hipStream_t stream) {
     if (a.max_splits > 1) {
         char* ws = static_cast<char*>(workspace);
         a.ws_out = reinterpret_cast<float*>(ws);
         a.ws_lse = reinterpret_cast<float*>(ws + decode_ws_out_bytes(a.B, a.H, a.max_splits));
+        a.ws_fmt = reinterpret_cast<uint8_t*>(ws + decode_ws_out_bytes(a.B, a.H, a.max_splits) +
+                                              decode_ws_lse_bytes(a.B, a.H, a.max_splits));
     } else {
         a.ws_out = nullptr;
         a.ws_lse = nullptr;
+        a.ws_fmt = nullptr;
     }
     return hip_status(mla::launch_decode(a, stream), "decode launch");
 }
@@ -143,7 +147,8 @@ int mla_decode_num_splits(int seq_len, int max_splits) {
 
 size_t mla_decode_workspace_bytes(int B, int H, int max_splits) {
     if (max_splits <= 1 || B <= 0 || H <= 0) return 0;
-    return decode_ws_out_bytes(B, H, max_splits) + decode_ws_lse_bytes(B, H, max_splits);
+    return decode_ws_out_bytes(B, H, max_splits) + decode_ws_lse_bytes(B, H, max_splits) +
+           decode_ws_fmt_bytes(B, H, max_splits);
 }
 
 size_t mla_nvfp4_swizzled_scale_bytes(int64_t rows, int64_t scale_cols) {

@@ -65,6 +65,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // v_mfma_f32_16x16x32_f16, same lane layout as the bf16 form
 __device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
@@ -265,6 +266,7 @@ void decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
+    bool wide_seen = false;   // some tile of this split exceeded the single-pass bound
 
     auto compute = [&](int kbuf, int slot) {
         const uint16_t* ks = sm.ks[kbuf];
@@ -394,7 +396,9 @@ void decode_kernel(DecodeArgs p) {
         const u32x4 wb = *reinterpret_cast<const u32x4*>(&sm.wide[slot][4]);
         const u32x4 wo = wa | wb;
         // (the flags are the same in every lane: a uniform branch)
-        if (__builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u) {
+        const bool wide = __builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u;
+        wide_seen = wide_seen || wide;
+        if (wide) {
             f16x8 pl;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -456,13 +460,29 @@ void decode_kernel(DecodeArgs p) {
         return;
     }
 
-    // Split: write the partial; split_merge_kernel combines them.
+    // Split: write the partial; split_merge_kernel combines them.  When no
+    // tile of the split exceeded the latent bound (|V| <= 8), the partial
+    // (a convex combination of V rows) is within 8 in magnitude and is
+    // stored as fp16 (absolute rounding <= 2^-8) in the first half of its row.
     if (!has_head) return;
     const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + hq;
     float* dst = p.ws_out + row * kLatent;
-    if (gq == 0) p.ws_lse[row] = lse_v;
+    if (gq == 0) {
+        p.ws_lse[row] = lse_v;
+        p.ws_fmt[row] = wide_seen ? 0 : 1;
+    }
+    if (!wide_seen) {
+        _Float16* dh = reinterpret_cast<_Float16*>(dst);
 #pragma unroll
-    for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+        for (int c = 0; c < 32; ++c) {
+            const f32x4 v = o[c] * so;
+            *reinterpret_cast<f16x4*>(dh + 16 * c + 4 * gq) =
+                f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+    }
 }
 
 // Merge of the split partials of a decode launch, one wavefront per (b, h)
@@ -495,9 +515,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
     for (int s = 0; s < ns; ++s) {
         const int64_t row = row0 + (int64_t)s * p.H;
         const float l = p.ws_lse[row];
-        const float* src = p.ws_out + row * kLatent + 8 * lane;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        f32x4 x0, x1;
+        if (p.ws_fmt[row]) {   // fp16 partial in the row's first half
+            const f16x8 h = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.ws_out + row * kLatent) + 8 * lane);
+            x0 = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+            x1 = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+        } else {
+            const float* src = p.ws_out + row * kLatent + 8 * lane;
+            x0 = *reinterpret_cast<const f32x4*>(src);
+            x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        }
         if (l == -INFINITY) continue;
         const float wgt = expf(l - M);
         wsum += wgt;

@@ -58,6 +58,7 @@ constexpr float kSinglePBound = 8.0f;
 struct NarrowSmem {
     _Float16 vt[kNW][kNT * kVP];  // 4 x 33,792 B; reused for the output merge
     float m[kNW][16], l[kNW][16];
+    uint32_t wide[kNW];           // wavefront w saw a tile above the single-pass bound
 };
 
 __device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
@@ -180,6 +181,7 @@ void decode_narrow_kernel(DecodeArgs p) {
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
+    bool wide_seen = false;   // some tile of this wavefront exceeded the single-pass bound
     _Float16* vt = sm.vt[w];
 
     // one tile: halves h2 = 0, 1 (tokens 16 h2 .. +15 of the tile)
@@ -323,6 +325,7 @@ void decode_narrow_kernel(DecodeArgs p) {
         };
         pv_sweep(ph);
         if (residual) pv_sweep(pl);
+        wide_seen = wide_seen || residual;
     };
 
     // ---- token loop: records of tile j+1 in flight, page-table entries of
@@ -365,6 +368,7 @@ void decode_narrow_kernel(DecodeArgs p) {
         sm.m[w][c16] = m_run;
         sm.l[w][c16] = l_run;
     }
+    if (lane == 0) sm.wide[w] = wide_seen ? 1u : 0u;
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
@@ -411,9 +415,26 @@ void decode_narrow_kernel(DecodeArgs p) {
         dst = p.out + ((int64_t)b * p.H + c16) * kLatent;
         if (gq == 0) p.lse[(int64_t)b * p.H + c16] = lse_v;
     } else {
+        // split partial: fp16 in the first half of its row when no tile of
+        // the split exceeded the latent bound (|partial| <= 8, absolute
+        // rounding <= 2^-8), fp32 otherwise
         const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + c16;
+        const bool wide = (sm.wide[0] | sm.wide[1] | sm.wide[2] | sm.wide[3]) != 0u;
         dst = p.ws_out + row * kLatent;
-        if (gq == 0) p.ws_lse[row] = lse_v;
+        if (gq == 0) {
+            p.ws_lse[row] = lse_v;
+            p.ws_fmt[row] = wide ? 0 : 1;
+        }
+        if (!wide) {
+            _Float16* dh = reinterpret_cast<_Float16*>(dst);
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                const f32x4 v = o[c] * so;
+                *reinterpret_cast<f16x4*>(dh + 16 * c + 4 * gq) =
+                    f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+            }
+            return;
+        }
     }
 #pragma unroll
     for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;

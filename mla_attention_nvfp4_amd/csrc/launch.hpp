@@ -29,8 +29,9 @@ struct DecodeArgs {
     int B, H;
     float outer_scale, softmax_scale;
     int max_splits;
-    float* ws_out;            // [B][max_splits][H][512] (null if max_splits == 1)
+    float* ws_out;            // [B][max_splits][H][512] fp32, or fp16 in the row's first half (null if max_splits == 1)
     float* ws_lse;            // [B][max_splits][H]
+    uint8_t* ws_fmt;          // [B][max_splits][H]: 1 = that partial row is fp16, 0 = fp32
     float* out;               // [B][H][512]
     float* lse;               // [B][H]
 };

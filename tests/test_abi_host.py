@@ -37,7 +37,9 @@ def test_constants_and_policy():
             k = L.decode_num_splits(n, s)
             tiles = (n + 63) // 64
             assert 1 <= k <= s and k <= tiles
-    assert L.decode_workspace_bytes(64, 128, 4) == 64 * 4 * 128 * 512 * 4 + 64 * 4 * 128 * 4
+    # fp32 partial rows, fp32 partial LSE, one format byte per row (256-B aligned regions)
+    assert L.decode_workspace_bytes(64, 128, 4) == 64 * 4 * 128 * 512 * 4 + 64 * 4 * 128 * 4 + 64 * 4 * 128
+    assert L.decode_workspace_bytes(3, 5, 2) == 256 * ((3 * 2 * 5 * 2048 + 255) // 256) + 256 + 256
     assert L.decode_workspace_bytes(64, 128, 1) == 0
     assert L.swizzled_scale_bytes(1, 1) == 128 * 4
     assert L.swizzled_scale_bytes(129, 1024) == 256 * 1024
