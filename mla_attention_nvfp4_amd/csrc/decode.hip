@@ -429,19 +429,16 @@ void decode_kernel(DecodeArgs p) {
                 pg_cur = page_of(pos_cur);            // issued now, used at the end
                 pos_next = position_of(t + 4);
             }
-            // The two halves of the workgroup run the phases in opposite
-            // order, so that each SIMD holds one wavefront in its MFMA phase
-            // while the other dequantizes.
-            const bool late = w >= NW / 2;
-            if (late && t + 1 < T1) {
+            // Dequant first, so that the records of tile t+2 are issued at
+            // the start of the iteration and have the whole compute phase of
+            // tile t (and the barrier) to land.  (Running the two halves of
+            // the workgroup in opposite phase order measured slower: the
+            // late-issued loads of one half then held the barrier.)
+            if (t + 1 < T1) {
                 dequant((i + 1) & 1, (i + 1) & 3);
-                if (t + 2 < T1) load_raw((i + 2) & 3);   // lands during tile t+1
+                if (t + 2 < T1) load_raw((i + 2) & 3);   // lands during tile t
             }
             if (wave_active) compute(i & 1, i & 3);
-            if (!late && t + 1 < T1) {
-                dequant((i + 1) & 1, (i + 1) & 3);
-                if (t + 2 < T1) load_raw((i + 2) & 3);
-            }
             if (w == 0 && t + 3 < T1) store_offs((i + 3) & 3, offset_of(pos_cur, pg_cur));
             lds_barrier();
         }
