@@ -62,28 +62,29 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t x) {
 
 // ---------------------------------------------------------------- e2m1 --
 
-// e2m1 code of an fp32 value: RNE, saturating at 6, sign bit kept.  The code
-// of |q| counts the midpoints it passes; ties sit on the even side.
-__device__ __forceinline__ uint32_t e2m1_encode(float q) {
-    const uint32_t s = (f2u(q) >> 28) & 8u;
-    const float a = __builtin_fabsf(q);
-    uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-                 (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-    return s | m;
+// e2m1 codes of a and b written as byte kSel of w (a in the low nibble) by
+// the gfx950 FP4 conversion with a unit scale: round to nearest, ties to
+// even (tied values go to the even code: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1,
+// 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturating at 6, sign bit kept also
+// when the result is 0.  Checked on the device against a comparison-based
+// encoder of that rule over all bf16 bit patterns, infinities included,
+// times a set of scale factors: no difference (NaN inputs are unspecified).
+template <int kSel>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t w, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, kSel);
 }
 
-// Twice the magnitude of e2m1 code & 7, as 4-bit fields of one word.
-constexpr uint32_t kE2m1TwiceMag = 0xC8643210u;
-
-// fp32 value of an e2m1 code (bit 3 sign).
-__device__ __forceinline__ float e2m1_decode(uint32_t c) {
-    const float mag = (float)((kE2m1TwiceMag >> ((c & 7u) * 4u)) & 0xfu) * 0.5f;
-    return (c & 8u) ? -mag : mag;
+// e2m1 codes of x[0..7] * s (each product one fp32 rounding), low nibble first.
+__device__ __forceinline__ uint32_t e2m1_encode8(const float* x, float s) {
+    uint32_t w = e2m1_pack2<0>(0u, x[0] * s, x[1] * s);
+    w = e2m1_pack2<1>(w, x[2] * s, x[3] * s);
+    w = e2m1_pack2<2>(w, x[4] * s, x[5] * s);
+    return e2m1_pack2<3>(w, x[6] * s, x[7] * s);
 }
 
 // Values of the two e2m1 codes in byte `sel` (0..3) of `w` (low nibble
 // first), by the gfx950 FP4 conversion with a unit scale (exact: checked
-// against e2m1_decode for all 256 bytes).
+// against the e2m1 value table for all 256 bytes).
 template <int kSel>
 __device__ __forceinline__ f32x2 e2m1_pair(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);

@@ -81,10 +81,11 @@ __global__ __launch_bounds__(256) void qk_qdq_kernel(const uint16_t* __restrict_
     u32x4 o0, o1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        o0[i] = pack_bf16_exact(e2m1_decode(e2m1_encode(v[2 * i] * sc.inv)) * sv,
-                                e2m1_decode(e2m1_encode(v[2 * i + 1] * sc.inv)) * sv);
-        o1[i] = pack_bf16_exact(e2m1_decode(e2m1_encode(v[8 + 2 * i] * sc.inv)) * sv,
-                                e2m1_decode(e2m1_encode(v[8 + 2 * i + 1] * sc.inv)) * sv);
+        // quantize-dequantize: codes by the FP4 conversion, values back exactly
+        const f32x2 d0 = e2m1_pair<0>(e2m1_pack2<0>(0u, v[2 * i] * sc.inv, v[2 * i + 1] * sc.inv));
+        const f32x2 d1 = e2m1_pair<0>(e2m1_pack2<0>(0u, v[8 + 2 * i] * sc.inv, v[8 + 2 * i + 1] * sc.inv));
+        o0[i] = pack_bf16_exact(d0[0] * sv, d0[1] * sv);
+        o1[i] = pack_bf16_exact(d1[0] * sv, d1[1] * sv);
     }
     u32x4* dst = reinterpret_cast<u32x4*>(out + (t * H + h) * kDqk + 16 * blk);
     dst[0] = o0;
@@ -123,11 +124,15 @@ __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__
     const Nvfp4Scale sc = nvfp4_block_scale(amax, g);
     const float sv = e4m3_decode(sc.code);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        if (i < cnt) {
-            const float q = e2m1_decode(e2m1_encode(x[i] * sc.inv)) * sv;
-            out[((int64_t)(t0 + i) * H + h) * kDv + d] =
-                kF16Out ? __builtin_bit_cast(uint16_t, (_Float16)q) : (uint16_t)(f2u(q) >> 16);
+    for (int i = 0; i < 16; i += 2) {
+        const f32x2 dq = e2m1_pair<0>(e2m1_pack2<0>(0u, x[i] * sc.inv, x[i + 1] * sc.inv));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (i + k < cnt) {
+                const float q = dq[k] * sv;
+                out[((int64_t)(t0 + i + k) * H + h) * kDv + d] =
+                    kF16Out ? __builtin_bit_cast(uint16_t, (_Float16)q) : (uint16_t)(f2u(q) >> 16);
+            }
         }
     }
 }
@@ -489,10 +494,8 @@ void attn_kernel(AttnParams p) {
         const Nvfp4Scale sc = nvfp4_block_scale(am, p.g_out);
         // codes of dims 16b + 4 g2 + 0..3 (bytes 2 g2, 2 g2 + 1) and
         // 16b + 8 + 4 g2 + 0..3 (bytes 4 + 2 g2, 5 + 2 g2)
-        const uint32_t c01 = e2m1_encode(x[0] * sc.inv) | (e2m1_encode(x[1] * sc.inv) << 4) |
-                             (e2m1_encode(x[2] * sc.inv) << 8) | (e2m1_encode(x[3] * sc.inv) << 12);
-        const uint32_t c23 = e2m1_encode(x[4] * sc.inv) | (e2m1_encode(x[5] * sc.inv) << 4) |
-                             (e2m1_encode(x[6] * sc.inv) << 8) | (e2m1_encode(x[7] * sc.inv) << 12);
+        const uint32_t c8 = e2m1_encode8(x, sc.inv);
+        const uint32_t c01 = c8 & 0xffffu, c23 = c8 >> 16;
         if (ok) {
             *reinterpret_cast<uint16_t*>(codes_row + 8 * b + 2 * g2) = (uint16_t)c01;
             *reinterpret_cast<uint16_t*>(codes_row + 8 * b + 4 + 2 * g2) = (uint16_t)c23;

@@ -42,9 +42,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
     const Nvfp4Scale sc = nvfp4_block_scale(a, g);
-    u32x2 w = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_encode(v[i] * sc.inv) << (4 * (i & 7));
+    const u32x2 w = {e2m1_encode8(v, sc.inv), e2m1_encode8(v + 8, sc.inv)};
     *reinterpret_cast<u32x2*>(codes + m * (K / 2) + 8 * c) = w;
     scales[so] = (uint8_t)sc.code;
 }
