@@ -201,6 +201,7 @@ int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_s
     a.num_pages = num_pages;
     a.record_bytes = record_bytes;
     a.page_size = page_size;
+    a.page_recip = mla::page_recip_of(page_size);
     a.page_table = page_table;
     a.max_pages = max_pages_per_seq;
     a.seq_lens = seq_lens;
@@ -240,6 +241,7 @@ int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int6
     a.num_pages = num_pages;
     a.record_bytes = record_bytes;
     a.page_size = page_size;
+    a.page_recip = mla::page_recip_of(page_size);
     a.page_table = page_table;
     a.max_pages = max_pages_per_seq;
     a.seq_lens = seq_lens;

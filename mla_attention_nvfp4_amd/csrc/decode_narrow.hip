@@ -155,12 +155,18 @@ void decode_narrow_kernel(DecodeArgs p) {
         return (j < nmine && item < i1 && pos >= 0 && pos < L) ? pos : -1;
     };
     auto page_of = [&](int pos) -> int {
-        const int pi = pos < 0 ? 0 : pos / p.page_size;
+        int pi, rem;
+        page_divmod(pos < 0 ? 0 : pos, p.page_size, p.page_recip, pi, rem);
         return p.page_table[(int64_t)b * p.max_pages + pi];
+    };
+    auto page_rem = [&](int pos) -> int {
+        int q, r;
+        page_divmod(pos < 0 ? 0 : pos, p.page_size, p.page_recip, q, r);
+        return r;
     };
     auto offset_of = [&](int pos, int pg) -> int64_t {
         return (pos >= 0 && pg >= 0 && pg < p.num_pages)
-                   ? ((int64_t)pg * p.page_size + pos % p.page_size) * kRec : int64_t(-1);
+                   ? ((int64_t)pg * p.page_size + page_rem(pos)) * kRec : int64_t(-1);
     };
     // masked tokens load record 0 (always present) and are zeroed at dequant
     auto load = [&](Staged& st, int64_t off) {

@@ -21,6 +21,7 @@ struct DecodeArgs {
     int64_t num_pages;
     int record_bytes;
     int page_size;
+    uint32_t page_recip;      // page_recip_of(page_size)
     const int32_t* page_table;
     int max_pages;
     const int32_t* seq_lens;
@@ -73,6 +74,26 @@ struct PrefillArgs {
 
 size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Division of a token position by the page size without an integer
+// division sequence: with r = min(floor(2^32 / d), 2^32 - 1) and
+// 0 <= n < 2^31, q0 = floor(n r / 2^32) satisfies n/d - 1 < q0 <= n/d
+// (n r / 2^32 >= n (2^32/d - 1) / 2^32 > n/d - 1), so one correction step
+// gives floor(n / d) and n mod d.
+__host__ __device__ inline uint32_t page_recip_of(int d) {
+    const uint64_t r = (uint64_t(1) << 32) / (uint64_t)(d < 1 ? 1 : d);
+    return r > 0xffffffffull ? 0xffffffffu : (uint32_t)r;
+}
+__device__ inline void page_divmod(int n, int d, uint32_t r, int& q, int& rem) {
+    uint32_t qq = __umulhi((uint32_t)n, r);
+    uint32_t rr = (uint32_t)n - qq * (uint32_t)d;
+    if (rr >= (uint32_t)d) {
+        ++qq;
+        rr -= (uint32_t)d;
+    }
+    q = (int)qq;
+    rem = (int)rr;
+}
 
 // Split policy shared by host and device code.
 __host__ __device__ inline int decode_num_splits(int n, int max_splits) {
