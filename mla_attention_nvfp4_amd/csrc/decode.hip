@@ -490,49 +490,95 @@ void decode_kernel(DecodeArgs p) {
 
 // Merge of the split partials of a decode launch, one wavefront per (b, h)
 // (same rule as lse_merge_kernel, splits in order); sequences with a single
-// split were written directly by the decode kernel.
+// split were written directly by the decode kernel.  Up to 64 splits, lane s
+// fetches split s's LSE and format byte together with the sequence length
+// (rows past the sequence's split count hold stale values and are masked
+// once the count is known), so the partial rows are read in a second round
+// of loads, four splits at a time.
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = wave_xor_max(v, m);
+    return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = wave_xor_sum(v, m);
+    return v;
+}
+
 template <bool kSparse>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wid >= p.B * p.H) return;
     const int b = wid / p.H, h = wid % p.H;
+    const int64_t row0 = (int64_t)b * p.max_splits * p.H + h;   // split s at row0 + s*H
+    float* dst = p.out + ((int64_t)b * p.H + h) * kLatent + 8 * lane;
+    const int64_t rl = row0 + (int64_t)(lane < p.max_splits ? lane : 0) * p.H;
+    const float lv = p.ws_lse[rl];
+    const uint32_t fv = p.ws_fmt[rl];
     int L = p.seq_lens[b];
     const int Lmax = p.max_pages * p.page_size;
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
     const int ns = decode_num_splits(kSparse ? p.topk : L, p.max_splits);
     if (ns <= 1) return;
-    const int64_t row0 = (int64_t)b * p.max_splits * p.H + h;   // split s at row0 + s*H
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_lse[row0 + (int64_t)s * p.H]);
-    float* dst = p.out + ((int64_t)b * p.H + h) * kLatent + 8 * lane;
-    if (M == -INFINITY) {
-        *reinterpret_cast<f32x4*>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (lane == 0) p.lse[(int64_t)b * p.H + h] = -INFINITY;
-        return;
-    }
-    float wsum = 0.0f;
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-        const int64_t row = row0 + (int64_t)s * p.H;
-        const float l = p.ws_lse[row];
-        f32x4 x0, x1;
-        if (p.ws_fmt[row]) {   // fp16 partial in the row's first half
-            const f16x8 h = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.ws_out + row * kLatent) + 8 * lane);
-            x0 = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-            x1 = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+    auto load_row = [&](int64_t row, bool f16, f32x4& x0, f32x4& x1) {
+        if (f16) {   // fp16 partial in the row's first half
+            const f16x8 v = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(p.ws_out + row * kLatent) + 8 * lane);
+            x0 = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+            x1 = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
         } else {
             const float* src = p.ws_out + row * kLatent + 8 * lane;
             x0 = *reinterpret_cast<const f32x4*>(src);
             x1 = *reinterpret_cast<const f32x4*>(src + 4);
         }
-        if (l == -INFINITY) continue;
-        const float wgt = expf(l - M);
-        wsum += wgt;
-        a0 += wgt * x0;
-        a1 += wgt * x1;
+    };
+    float M, wsum;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    if (ns <= 64) {
+        const float l = lane < ns ? lv : -INFINITY;
+        M = wave_max64(l);
+        const float wl = (l == -INFINITY || M == -INFINITY) ? 0.0f : expf(l - M);
+        wsum = wave_sum64(wl);
+        for (int s0 = 0; s0 < ns; s0 += 4) {
+            f32x4 x0[4], x1[4];
+            float wg[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sj = s0 + j < ns ? s0 + j : s0;   // (uniform)
+                wg[j] = __int_as_float(s0 + j < ns ? __builtin_amdgcn_readlane(__float_as_int(wl), sj) : 0);
+                const bool f16 = __builtin_amdgcn_readlane(fv, sj) != 0u;
+                load_row(row0 + (int64_t)sj * p.H, f16, x0[j], x1[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (wg[j] != 0.0f) {   // (uniform) splits past the count and those without tokens add nothing
+                    a0 += wg[j] * x0[j];
+                    a1 += wg[j] * x1[j];
+                }
+            }
+        }
+    } else {
+        M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_lse[row0 + (int64_t)s * p.H]);
+        wsum = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const int64_t row = row0 + (int64_t)s * p.H;
+            const float l = p.ws_lse[row];
+            if (l == -INFINITY) continue;
+            f32x4 x0, x1;
+            load_row(row, p.ws_fmt[row] != 0, x0, x1);
+            const float wgt = expf(l - M);
+            wsum += wgt;
+            a0 += wgt * x0;
+            a1 += wgt * x1;
+        }
+    }
+    if (M == -INFINITY) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (lane == 0) p.lse[(int64_t)b * p.H + h] = -INFINITY;
+        return;
     }
     const float inv = 1.0f / wsum;
     *reinterpret_cast<f32x4*>(dst) = a0 * inv;
