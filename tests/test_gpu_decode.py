@@ -58,6 +58,35 @@ def test_dense_pv_bound(case):
     compare(out, lse, ref_out, ref_lse, list(range(B)), f"pvbound{seed}")
 
 
+@pytest.mark.parametrize("H", [128, 16], ids=["wide", "narrow"])
+def test_dense_mixed_partial_formats(H):
+    """Outliers only in the first 300 positions of each sequence: the first
+    split exceeds the latent bound (fp32 partial), the later ones do not
+    (fp16 partials), and the merge sees both formats in one sequence."""
+    inp = workloads.small_decode(40 + H, 2, H, [2048, 1500], page_size=64, rec=432, max_splits=4)
+    g = torch.Generator().manual_seed(41)
+    for b in range(inp.B):
+        r0 = int(inp.token_offsets[b])
+        blk = inp.kv_c[r0:r0 + 300]
+        hit = torch.rand(blk.shape, generator=g) < 0.01
+        blk[hit] = (blk[hit].to(torch.float32) * 20).to(torch.bfloat16)
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, list(range(inp.B)))
+    compare(out, lse, ref_out, ref_lse, list(range(inp.B)), f"mixed-formats-H{H}")
+
+
+@pytest.mark.parametrize("H", [32, 8], ids=["wide", "narrow"])
+def test_dense_more_than_64_splits(H):
+    """67 splits of one sequence: the merge's path for more splits than lanes."""
+    inp = workloads.small_decode(50 + H, 1, H, [17000], page_size=64, rec=368, max_splits=80)
+    assert ops.decode_num_splits(17000, 80) == 67
+    cache = gpu_cache(inp)
+    out, lse = gpu_decode(inp, cache)
+    ref_out, ref_lse = oracle_decode(inp, [0])
+    compare(out, lse, ref_out, ref_lse, [0], f"67-splits-H{H}")
+
+
 SMALL_SPARSE = [
     # seed, B, H, lens, topk, invalid_frac, splits
     (11, 3, 16, [100, 0, 700], 96, 0.1, 1),
