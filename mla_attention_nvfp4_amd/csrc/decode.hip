@@ -97,7 +97,9 @@ void decode_kernel(DecodeArgs p) {
     static_assert(NW == 8, "the per-tile flags are read as two 4-word vectors");
     __shared__ DecodeSmem<NW> sm;
 
-    const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    int s, u;
+    decode_work_item(p.max_splits, p.B * (int)gridDim.z, s, u);
+    const int b = u % p.B, hg = u / p.B;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, c16 = lane & 15;
 
@@ -491,10 +493,12 @@ void decode_kernel(DecodeArgs p) {
 // Merge of the split partials of a decode launch, one wavefront per (b, h)
 // (same rule as lse_merge_kernel, splits in order); sequences with a single
 // split were written directly by the decode kernel.  Up to 64 splits, lane s
-// fetches split s's LSE and format byte together with the sequence length
-// (rows past the sequence's split count hold stale values and are masked
-// once the count is known), so the partial rows are read in a second round
-// of loads, four splits at a time.
+// fetches split s's LSE and format byte together with the sequence length,
+// and the fp16 partial rows of the first four splits are loaded in the same
+// round (every row exists, and fp16 is the usual format); rows past the
+// sequence's split count hold stale values and are masked once the count is
+// known.  A split stored as fp32 is re-read, and further splits are read
+// four at a time.
 __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) v = wave_xor_max(v, m);
@@ -517,6 +521,11 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
     const int64_t rl = row0 + (int64_t)(lane < p.max_splits ? lane : 0) * p.H;
     const float lv = p.ws_lse[rl];
     const uint32_t fv = p.ws_fmt[rl];
+    f16x8 spec[4];   // fp16 rows of splits 0..3, loaded before the split count is known
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        spec[j] = *reinterpret_cast<const f16x8*>(
+            reinterpret_cast<const _Float16*>(p.ws_out + (row0 + (int64_t)(j < p.max_splits ? j : 0) * p.H) * kLatent) + 8 * lane);
     int L = p.seq_lens[b];
     const int Lmax = p.max_pages * p.page_size;
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -545,10 +554,17 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
             float wg[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int sj = s0 + j < ns ? s0 + j : s0;   // (uniform)
-                wg[j] = __int_as_float(s0 + j < ns ? __builtin_amdgcn_readlane(__float_as_int(wl), sj) : 0);
+                const bool in = s0 + j < ns;
+                const int sj = in ? s0 + j : s0;   // (uniform)
+                wg[j] = __int_as_float(in ? __builtin_amdgcn_readlane(__float_as_int(wl), sj) : 0);
                 const bool f16 = __builtin_amdgcn_readlane(fv, sj) != 0u;
-                load_row(row0 + (int64_t)sj * p.H, f16, x0[j], x1[j]);
+                if (s0 == 0 && f16 && in) {
+                    const f16x8 v = spec[j];
+                    x0[j] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+                    x1[j] = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+                } else {
+                    load_row(row0 + (int64_t)sj * p.H, f16, x0[j], x1[j]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {

@@ -82,7 +82,8 @@ void decode_narrow_kernel(DecodeArgs p) {
     constexpr int kRec = kRopeFp8 ? 368 : 432;
     __shared__ NarrowSmem sm;
 
-    const int s = blockIdx.x, b = blockIdx.y;
+    int s, b;
+    decode_work_item(p.max_splits, p.B, s, b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, gq = lane >> 4;
 

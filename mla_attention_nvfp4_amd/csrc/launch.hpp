@@ -95,6 +95,25 @@ __device__ inline void page_divmod(int n, int d, uint32_t r, int& q, int& rem) {
     rem = (int)rr;
 }
 
+// XCD-aware placement of decode work items.  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2) in linear-id order.
+// When the number N of (sequence, head group) units is a multiple of 8, the
+// linear id L maps to unit u = x + 8 (k / S) and split s = k % S, with
+// x = L % 8 and k = L / 8, so that all S splits of a unit run on XCD u % 8
+// and share that L2 for Q and the page table; this is a bijection of
+// [0, S N) onto [0, S) x [0, N).  Otherwise u = L / S and s = L % S.
+__device__ inline void decode_work_item(int S, int N, int& s, int& u) {
+    const int L = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    if ((N & 7) == 0) {
+        const int k = L >> 3;
+        u = (L & 7) + 8 * (k / S);
+        s = k % S;
+    } else {
+        s = L % S;
+        u = L / S;
+    }
+}
+
 // Split policy shared by host and device code.
 __host__ __device__ inline int decode_num_splits(int n, int max_splits) {
     if (n <= 0) return 1;
