@@ -103,7 +103,25 @@ void decode_kernel(DecodeArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, c16 = lane & 15;
 
+    const int h_base = hg * (16 * NW) + 16 * w;
+    const bool wave_active = h_base < p.H;
+    const int hq = h_base + c16;
+
+    // The sequence length and this wavefront's Q rows are requested
+    // together (the length first, so that it can be waited for alone); the
+    // page-table entries of the first tiles are requested before Q is
+    // processed.
     int L = p.seq_lens[b];
+    const bool qok = hq < p.H;
+    const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(qok ? hq : 0) * p.q_stride_h + 8 * gq;
+    u32x4 qraw[16], qrope[2];
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) qraw[kk] = qok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) qrope[kk] = qok ? *reinterpret_cast<const u32x4*>(p.q_rope + qoff + 32 * kk) : zero;
+    }
     const int Lmax = p.max_pages * p.page_size;
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
     const int n_items = kSparse ? p.topk : L;
@@ -112,10 +130,6 @@ void decode_kernel(DecodeArgs p) {
     const int ct = decode_chunk_tiles(n_items, p.max_splits);  // in 64-token tiles
     const int T0 = 2 * s * ct;
     const int T1 = min((n_items + kTile - 1) / kTile, T0 + 2 * ct);
-
-    const int h_base = hg * (16 * NW) + 16 * w;
-    const bool wave_active = h_base < p.H;
-    const int hq = h_base + c16;
 
     // Q as the B operand of S^T = K Q^T: k-step kk covers d = 32kk..32kk+31
     // (kk 16, 17: RoPE).  Latent k-steps are fp16, scaled by 2^(14 - E)
@@ -126,19 +140,13 @@ void decode_kernel(DecodeArgs p) {
     // for kk < kQLdsLatent, kQLdsLatent + kk - 16 for RoPE).
     f16x8 qf[16 - kQLdsLatent];
     float q_unscale;   // 2^(E - 14)
-    {
-        const bool ok = hq < p.H;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(ok ? hq : 0) * p.q_stride_h + 8 * gq;
-        u32x4 raw[16];
+    auto setup_q = [&]() {
         float amax = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            raw[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q_nope + qoff + 32 * kk) : zero;
+        for (int kk = 0; kk < 16; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(raw[kk][j])), __builtin_fabsf(bf16_hi(raw[kk][j]))));
-        }
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(qraw[kk][j])), __builtin_fabsf(bf16_hi(qraw[kk][j]))));
         amax = xor32_max(xor16_max(amax));   // over the head's four lanes c16 + 16gq
         int E = amax > 0.0f ? (int)((f2u(amax) >> 23) & 0xffu) - 127 : 0;
         E = E < -100 ? -100 : E;
@@ -149,20 +157,19 @@ void decode_kernel(DecodeArgs p) {
             f16x8 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(raw[kk][j]), sh);
-                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(raw[kk][j]), sh);
+                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(qraw[kk][j]), sh);
+                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(qraw[kk][j]), sh);
             }
             if (kk < kQLdsLatent) sm.qs[w][kk][lane] = __builtin_bit_cast(u32x4, v);
             else qf[kk - kQLdsLatent] = v;
         }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            sm.qs[w][kQLdsLatent + kk][lane] = ok ? *reinterpret_cast<const u32x4*>(p.q_rope + qoff + 32 * kk) : zero;
-    }
+        for (int kk = 0; kk < 2; ++kk) sm.qs[w][kQLdsLatent + kk][lane] = qrope[kk];
+    };
 
     const uint8_t* __restrict__ cache = p.cache;
     const float outer = p.outer_scale;
-    const float lat_scale = outer * q_unscale;            // latent partial sum -> outer * q.k
+    float lat_scale = 0.0f;                               // latent partial sum -> outer * q.k (set with Q)
     const float score_scale = p.softmax_scale * kLog2e;   // log2 units
     const float wide_scale = kSinglePBound / (6.0f * outer);   // block scales above this need the residual pass
 
@@ -417,10 +424,22 @@ void decode_kernel(DecodeArgs p) {
     };
 
     if (T0 < T1) {
-        if (w == 0) {
-            compute_offs(T0, 0);
-            if (T0 + 1 < T1) compute_offs(T0 + 1, 1);
-            if (T0 + 2 < T1) compute_offs(T0 + 2, 2);
+        {
+            // page-table entries of tiles T0..T0+2 requested by every
+            // wavefront (uniform control flow), Q processed meanwhile
+            int pos0[3], pg0[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                pos0[k] = T0 + k < T1 ? position_of(T0 + k) : -1;
+                pg0[k] = page_of(pos0[k]);
+            }
+            setup_q();
+            lat_scale = outer * q_unscale;
+            if (w == 0) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    if (T0 + k < T1) store_offs(k, offset_of(pos0[k], pg0[k]));
+            }
         }
         __syncthreads();
         load_raw(0);

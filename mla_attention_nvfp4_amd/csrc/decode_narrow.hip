@@ -87,7 +87,21 @@ void decode_narrow_kernel(DecodeArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, gq = lane >> 4;
 
+    // The sequence length and Q are requested together (the length first,
+    // so that it can be waited for alone); the page-table entries of the
+    // first tiles are requested before Q is processed.
+    const bool hok = c16 < p.H;
     int L = p.seq_lens[b];
+    u32x4 qraw[16], qrraw[2];
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const uint16_t* qn = p.q_nope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 128 * gq;
+        const uint16_t* qp = p.q_rope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 16 * gq;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) qraw[kk] = hok ? *reinterpret_cast<const u32x4*>(qn + 8 * kk) : zero;
+#pragma unroll
+        for (int kr = 0; kr < 2; ++kr) qrraw[kr] = hok ? *reinterpret_cast<const u32x4*>(qp + 8 * kr) : zero;
+    }
     const int Lmax = p.max_pages * p.page_size;
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
     const int n_items = kSparse ? p.topk : L;
@@ -99,8 +113,6 @@ void decode_narrow_kernel(DecodeArgs p) {
     const int ntiles = (i1 - i0 + kNT - 1) / kNT;
     const int nmine = ntiles > w ? (ntiles - w + kNW - 1) / kNW : 0;   // tiles w, w+4, ...
 
-    const bool hok = c16 < p.H;
-
     // ---- Q.  Latent (B operand of the fp16 k-steps): lane holds head c16,
     // dims 128gq + 8kk .. +7 for kk = 0..15, scaled by 2^(14 - E) where 2^E
     // <= max |q_nope| of the head < 2^(E+1) (exact; the largest value lands
@@ -108,19 +120,13 @@ void decode_narrow_kernel(DecodeArgs p) {
     f16x8 qf[16];
     bf16x8 qr[2];
     float q_unscale;   // 2^(E - 14)
-    {
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        const uint16_t* qn = p.q_nope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 128 * gq;
-        const uint16_t* qp = p.q_rope + (int64_t)b * p.q_stride_b + (int64_t)(hok ? c16 : 0) * p.q_stride_h + 16 * gq;
-        u32x4 raw[16];
+    auto setup_q = [&]() {
         float amax = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            raw[kk] = hok ? *reinterpret_cast<const u32x4*>(qn + 8 * kk) : zero;
+        for (int kk = 0; kk < 16; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(raw[kk][j])), __builtin_fabsf(bf16_hi(raw[kk][j]))));
-        }
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(qraw[kk][j])), __builtin_fabsf(bf16_hi(qraw[kk][j]))));
         amax = xor32_max(xor16_max(amax));
         int E = amax > 0.0f ? (int)((f2u(amax) >> 23) & 0xffu) - 127 : 0;
         E = E < -100 ? -100 : E;
@@ -131,19 +137,19 @@ void decode_narrow_kernel(DecodeArgs p) {
             f16x8 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(raw[kk][j]), sh);
-                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(raw[kk][j]), sh);
+                v[2 * j] = (_Float16)__builtin_ldexpf(bf16_lo(qraw[kk][j]), sh);
+                v[2 * j + 1] = (_Float16)__builtin_ldexpf(bf16_hi(qraw[kk][j]), sh);
             }
             qf[kk] = v;
         }
 #pragma unroll
-        for (int kr = 0; kr < 2; ++kr) qr[kr] = as_bf16x8(hok ? *reinterpret_cast<const u32x4*>(qp + 8 * kr) : zero);
-    }
+        for (int kr = 0; kr < 2; ++kr) qr[kr] = as_bf16x8(qrraw[kr]);
+    };
 
     const uint8_t* __restrict__ cache = p.cache;
     const float outer = p.outer_scale;
     const float sc_rope = p.softmax_scale * kLog2e;
-    const float sc_lat = sc_rope * outer * q_unscale;
+    float sc_lat = 0.0f;   // set with Q
     const float wide_scale = kSinglePBound / (6.0f * outer);   // block scales above this need the residual sweep
 
     // ---- token addressing: tile j of this wavefront covers items
@@ -341,11 +347,20 @@ void decode_narrow_kernel(DecodeArgs p) {
         Staged cur[2], nxt[2];
         int64_t offA[2], offB[2];
         int posC[2];
+        int p0[2], p1[2], g0[2], g1[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const int p0 = position_of(0, h2), p1 = position_of(1, h2);
-            offA[h2] = offset_of(p0, page_of(p0));
-            offB[h2] = offset_of(p1, page_of(p1));
+            p0[h2] = position_of(0, h2);
+            p1[h2] = position_of(1, h2);
+            g0[h2] = page_of(p0[h2]);
+            g1[h2] = page_of(p1[h2]);
+        }
+        setup_q();
+        sc_lat = sc_rope * outer * q_unscale;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            offA[h2] = offset_of(p0[h2], g0[h2]);
+            offB[h2] = offset_of(p1[h2], g1[h2]);
             posC[h2] = position_of(2, h2);
         }
         load(cur[0], offA[0]);
