@@ -9,8 +9,9 @@ kernel).  Inputs are
 resident in HBM before timing starts; the cache is rotated over 4 copies
 (> 256 MB Infinity Cache) so that decode reads come from HBM.
 
-Printed: one JSON line with queries/s (B / step time), the roofline of the
-decode call (HIP events around every timed call, on the launch stream),
+Printed: one JSON line with queries/s (B / step time, host clock), the
+roofline of the decode call (a second timed region of back-to-back decode
+calls between one pair of HIP events on the launch stream),
 the oracle's CPU throughput on a bounded sample, and extra lines for the
 other paths (16-head decode, top-k sparse decode, prefill).
 
@@ -108,26 +109,34 @@ class DecodeBench:
                               workspace=self.ws)
 
     def run(self, steps: int, warmup: int, with_write: bool = True):
-        """Returns (ms per step from the host clock, mean decode-kernel ms from HIP events)."""
+        """Returns (ms per step from the host clock, mean decode-call ms from HIP events).
+
+        Two timed regions: `steps` serving steps (cache write + decode call)
+        on the host clock, then `steps` decode calls back to back between one
+        pair of HIP events on the launch stream, whose mean is the call's
+        launch-to-launch duration (kernels and the gap between them, without
+        the few microseconds an event pair around every call would add)."""
         stream = torch.cuda.current_stream()
         for i in range(warmup):
             if with_write:
                 self.write(i % self.n_rot)
             self.decode(i % self.n_rot)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             r = i % self.n_rot
             if with_write:
                 self.write(r)
-            ev[i][0].record(stream)
             self.decode(r)
-            ev[i][1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        k_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-        return (t1 - t0) * 1e3 / steps, k_ms
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(steps):
+            self.decode(i % self.n_rot)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_B64_H128_L4096_hbm_bytes.md")
@@ -155,18 +164,19 @@ def measured_traffic():
 
 
 def timed(fn, steps: int, warmup: int) -> float:
-    """Mean ms of fn() over `steps` launches, HIP events on the current stream."""
+    """Mean ms of fn() over `steps` back-to-back launches between one pair of
+    HIP events on the current stream."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
-    for a, b in ev:
-        a.record(stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    return ev0.elapsed_time(ev1) / steps
 
 
 def bench_cache_write(inp, steps: int, warmup: int) -> dict:
