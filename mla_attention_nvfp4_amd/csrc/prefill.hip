@@ -214,11 +214,16 @@ void attn_kernel(AttnParams p) {
         const float d = e4m3_decode(threadIdx.x) * p.g_p;
         sm.pinv[threadIdx.x] = (d == 0.0f) ? 0.0f : 1.0f / d;
     }
-    const int n = blockIdx.z, h = blockIdx.y;
+    // XCD-aware placement (as for decode): all query tiles of one (sequence,
+    // head) run on one XCD when 8 divides the number of (sequence, head)
+    // pairs, so that they stream the same K/V tiles through one L2
+    int qx, u;
+    decode_work_item((int)gridDim.x, (int)(gridDim.y * gridDim.z), qx, u);
+    const int h = u % (int)gridDim.y, n = u / (int)gridDim.y;
     const int a = p.cu[n], e = p.cu[n + 1];
     const int L = e - a;
     const int nqt = (L + kBM - 1) / kBM;
-    const int qt = nqt - 1 - (int)blockIdx.x;   // longest (latest) tiles first
+    const int qt = nqt - 1 - qx;   // longest (latest) tiles first
     if (qt < 0) return;
     const int r0 = qt * kBM;                     // local row of the tile
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
