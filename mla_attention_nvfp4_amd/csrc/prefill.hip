@@ -94,7 +94,8 @@ __global__ __launch_bounds__(256) void qk_qdq_kernel(const uint16_t* __restrict_
 
 // ------------------------------------------------------------------- V --
 
-// grid (ceil(max_seqlen/16), N, ceil(H*128/256)); thread = (head, dim)
+// grid (ceil(max_seqlen/16), N, ceil(H*128/8/256)); thread = (head, 8 dims):
+// 16 tokens x 8 dims in 16-byte loads and stores, eight blocks per thread.
 // kF16Out: the exact values s*v are written as fp16 (they fit: at most 6
 // significant bits, magnitudes in [2^-10, 2688]) for the fp16 PV products,
 // otherwise as bf16.
@@ -106,34 +107,46 @@ __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__
     const int a = cu[n], e = cu[n + 1];
     const int t0 = a + 16 * blockIdx.x;
     if (t0 >= e) return;
-    const int hd = blockIdx.z * 256 + threadIdx.x;
-    if (hd >= H * kDv) return;
-    const int h = hd / kDv, d = hd % kDv;
+    const int hd8 = blockIdx.z * 256 + threadIdx.x;
+    if (hd8 >= H * (kDv / 8)) return;
+    const int h = hd8 / (kDv / 8), d0 = 8 * (hd8 % (kDv / 8));
     const int cnt = min(16, e - t0);
-    float x[16];
-    float amax = 0.0f;
+    u32x4 raw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        x[i] = 0.0f;
-        if (i < cnt) {
-            const uint16_t bits = v[(int64_t)(t0 + i) * st + (int64_t)h * sh + d];
-            x[i] = u2f((uint32_t)bits << 16);
-            amax = fmaxf(amax, __builtin_fabsf(x[i]));
-        }
+        const int ti = t0 + min(i, cnt - 1);   // (rows past the sequence end are not used)
+        raw[i] = *reinterpret_cast<const u32x4*>(v + (int64_t)ti * st + (int64_t)h * sh + d0);
     }
-    const Nvfp4Scale sc = nvfp4_block_scale(amax, g);
-    const float sv = e4m3_decode(sc.code);
+    // x[i][j]: token t0 + i, dim d0 + j (tokens past the end are 0)
+    auto x_of = [&](int i, int j) -> float {
+        const uint32_t w = raw[i][j >> 1];
+        return i < cnt ? ((j & 1) ? bf16_hi(w) : bf16_lo(w)) : 0.0f;
+    };
+    uint32_t res[16][4];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-        const f32x2 dq = e2m1_pair<0>(e2m1_pack2<0>(0u, x[i] * sc.inv, x[i + 1] * sc.inv));
+    for (int j = 0; j < 8; ++j) {
+        float amax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (i + k < cnt) {
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(x_of(i, j)));
+        const Nvfp4Scale sc = nvfp4_block_scale(amax, g);
+        const float sv = e4m3_decode(sc.code);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const f32x2 dq = e2m1_pair<0>(e2m1_pack2<0>(0u, x_of(i, j) * sc.inv, x_of(i + 1, j) * sc.inv));
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
                 const float q = dq[k] * sv;
-                out[((int64_t)(t0 + i + k) * H + h) * kDv + d] =
-                    kF16Out ? __builtin_bit_cast(uint16_t, (_Float16)q) : (uint16_t)(f2u(q) >> 16);
+                const uint32_t bits = kF16Out ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q) : (f2u(q) >> 16);
+                uint32_t& word = res[i + k][j >> 1];
+                word = (j & 1) ? ((word & 0xffffu) | (bits << 16)) : bits;
             }
         }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i < cnt)
+            *reinterpret_cast<u32x4*>(out + ((int64_t)(t0 + i) * H + h) * kDv + d0) =
+                u32x4{res[i][0], res[i][1], res[i][2], res[i][3]};
     }
 }
 
@@ -560,7 +573,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         ws += (size_t)T * H * kDqk;
     }
     if (a.flags & 8u) {
-        const dim3 grid((unsigned)((a.max_seqlen + 15) / 16), (unsigned)a.N, (unsigned)((H * kDv + 255) / 256));
+        const dim3 grid((unsigned)((a.max_seqlen + 15) / 16), (unsigned)a.N, (unsigned)((H * (kDv / 8) + 255) / 256));
         if (a.flags & 4u)
             hipLaunchKernelGGL(v_qdq_kernel<true>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens, H,
                                a.g_v, ws);
