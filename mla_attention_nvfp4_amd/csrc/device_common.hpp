@@ -42,6 +42,14 @@ __device__ __forceinline__ uint32_t e4m3_encode(float t) {
     return sign | code;
 }
 
+// e4m3 code of t >= 0 by the gfx950 FP8 conversion (round to nearest even):
+// the same code as e4m3_encode for every fp32 value in [0, 448] (checked on
+// the device over all of them).  Larger values, +inf and NaN are clamped to
+// 448 first, whose code (0x7E) is the one e4m3_encode gives them.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float t) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xffu;
+}
+
 // fp32 value of an e4m3 code by the gfx950 FP8 conversion (OCP E4M3FN,
 // exact; codes 0x7F/0xFF are NaN and never produced by the encoders here).
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
@@ -104,7 +112,7 @@ struct Nvfp4Scale {
 __device__ __forceinline__ Nvfp4Scale nvfp4_block_scale(float a, float g) {
     const float u = 6.0f * g;
     const float t = a / u;
-    const uint32_t s = e4m3_encode(t);
+    const uint32_t s = e4m3_encode_nonneg(t);   // t >= 0 (or NaN)
     const float d = e4m3_decode(s) * g;
     return Nvfp4Scale{s, (d == 0.0f) ? 0.0f : 1.0f / d};
 }

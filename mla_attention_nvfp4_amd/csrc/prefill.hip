@@ -318,20 +318,26 @@ void attn_kernel(AttnParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- softmax: z in log2 units; the running max refreshed per tile
+        // (a tile without masked keys: the max is taken on the raw scores,
+        // since fp32(c x) is monotone in x for c >= 0, and each exponent is
+        // one fused c * s - m)
         float mx = -INFINITY;
 #pragma unroll
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                float z = c_log2 * s[mt2][v];
-                if (kMask) {
+                if constexpr (kMask) {
+                    float z = c_log2 * s[mt2][v];
                     const int key = kt * kBN + 32 * mt2 + 8 * (v >> 2) + 4 * g2 + (v & 3);
                     z = key <= row ? z : -INFINITY;
+                    s[mt2][v] = z;
+                    mx = fmaxf(mx, z);
+                } else {
+                    mx = fmaxf(mx, s[mt2][v]);
                 }
-                s[mt2][v] = z;
-                mx = fmaxf(mx, z);
             }
         mx = xor32_max(mx);
+        if constexpr (!kMask) mx = c_log2 * mx;
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -340,7 +346,8 @@ void attn_kernel(AttnParams p) {
         for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                s[mt2][v] = __builtin_amdgcn_exp2f(s[mt2][v] - m_use);
+                if constexpr (kMask) s[mt2][v] = __builtin_amdgcn_exp2f(s[mt2][v] - m_use);
+                else s[mt2][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(c_log2, s[mt2][v], -m_use));
                 psum += s[mt2][v];
             }
         psum = xor32_sum(psum);
@@ -378,11 +385,15 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) tq[kb] = nr[kb] ? am[kb] / p.u_p : tq[kb];
             }
+            // the four blocks' e4m3 codes by two hardware conversions (tq >= 0;
+            // see e4m3_encode_nonneg)
+            uint32_t codes4 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(tq[0], 448.0f), fminf(tq[1], 448.0f), 0, false);
+            codes4 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(tq[2], 448.0f), fminf(tq[3], 448.0f), (int)codes4, true);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const f32x16& t = s[kb >> 1];
                 const int o8 = 8 * (kb & 1);
-                const uint32_t code = e4m3_encode(tq[kb]);
+                const uint32_t code = (codes4 >> (8 * kb)) & 0xffu;
                 const float inv = sm.pinv[code];
                 const float sval = e4m3_decode(code);
                 uint32_t c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[o8] * inv, t[o8 + 1] * inv, 1.0f, 0);
