@@ -72,7 +72,9 @@ def _nearest_ties_even(a: np.ndarray, table: np.ndarray) -> np.ndarray:
     d_lo = np.abs(a - table[lo])
     d_hi = np.abs(table[hi] - a)
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    return np.where(pick_hi, hi, lo)
+    # above the largest entry the distances to the last two entries can round
+    # to the same float64 (huge a): saturation decides, not the distance
+    return np.where(a > table[-1], len(table) - 1, np.where(pick_hi, hi, lo))
 
 
 def e2m1_value(code) -> np.ndarray:

@@ -151,3 +151,17 @@ def test_ragged_blocks_equal_zero_padded():
     pad[:21] = x
     want = F.nvfp4_qdq(pad, 0.5, axis=0)[:21]
     assert np.array_equal(got, want)
+
+
+def test_encoders_saturate_far_above_range():
+    """Satfinite far above the largest magnitude (the quantizer reaches such
+    element values when a block's scale saturates at 448): e2m1 gives +-6
+    (codes 7 and 15), e4m3 gives +-448 (0x7E and 0xFE), for every float32
+    exponent above the range, up to the largest finite float32."""
+    big = np.float32(2.0) ** np.arange(3, 128, dtype=np.float32)
+    big = np.concatenate([big, [np.finfo(np.float32).max, np.float32(4.5535715e36)]]).astype(np.float32)
+    assert np.all(F.e2m1_encode(big) == 7)
+    assert np.all(F.e2m1_encode(-big) == 15)
+    big4 = big[big > 448]
+    assert np.all(F.e4m3_encode(big4) == 0x7E)
+    assert np.all(F.e4m3_encode(-big4) == 0xFE)
