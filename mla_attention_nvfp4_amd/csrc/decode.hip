@@ -100,7 +100,8 @@ void decode_kernel(DecodeArgs p) {
     int s, u;
     decode_work_item(p.max_splits, p.B * (int)gridDim.z, s, u);
     const int b = u % p.B, hg = u / p.B;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // (wavefront-uniform)
     const int gq = lane >> 4, c16 = lane & 15;
 
     const int h_base = hg * (16 * NW) + 16 * w;
@@ -180,7 +181,7 @@ void decode_kernel(DecodeArgs p) {
         const int item = t * kTile + (lane & (kTile - 1));
         const int ic = min(item, max(n_items - 1, 0));
         const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
-        return (item < n_items && pos >= 0 && pos < L) ? pos : -1;
+        return (t < T1 && item < n_items && pos >= 0 && pos < L) ? pos : -1;   // (tiles past the split: masked)
     };
     auto page_of = [&](int pos) -> int {
         int pi, rem;
@@ -321,6 +322,13 @@ void decode_kernel(DecodeArgs p) {
                 sa[0] = mfma16x16x32(as_bf16x8(f0[kk & 1]), qv, sa[0]);
                 sa[1] = mfma16x16x32(as_bf16x8(f1[kk & 1]), qv, sa[1]);
             }
+            // the next k-step's LDS reads are issued ahead of this step's
+            // two products
+            if (kk + 1 < 18) {
+                if (q_lds(kk + 1)) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores (log2 units) of tokens 16tt + 4gq + i for head c16
@@ -401,6 +409,10 @@ void decode_kernel(DecodeArgs p) {
                 }
                 o[c] = mfma_k32_f16(va, pp, o[c]);
                 o[c + 1] = mfma_k32_f16(vb, pp, o[c + 1]);
+                if (c + 2 < 32) {   // the next fragments' reads ahead of these products
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 va = na;
                 vb = nb;
@@ -430,43 +442,42 @@ void decode_kernel(DecodeArgs p) {
             int pos0[3], pg0[3];
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                pos0[k] = T0 + k < T1 ? position_of(T0 + k) : -1;
+                pos0[k] = position_of(T0 + k);
                 pg0[k] = page_of(pos0[k]);
             }
             setup_q();
             lat_scale = outer * q_unscale;
             if (w == 0) {
 #pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    if (T0 + k < T1) store_offs(k, offset_of(pos0[k], pg0[k]));
+                for (int k = 0; k < 3; ++k) store_offs(k, offset_of(pos0[k], pg0[k]));
             }
         }
         __syncthreads();
         load_raw(0);
         dequant(0, 0);
-        if (T0 + 1 < T1) load_raw(1);
+        load_raw(1);
         int pos_next = position_of(T0 + 3);
         __syncthreads();
         for (int t = T0; t < T1; ++t) {
             const int i = t - T0;
-            // wavefront 0 resolves tile t+3 in two stages (see above)
+            // tile t+3 in two stages: its page-table entry is requested now
+            // and its offsets stored at the end.  Every wavefront issues the
+            // same loads every iteration (tiles past the split are masked and
+            // read record 0), so the compiler's load counters stay exact and
+            // the wait for the page-table entry does not also wait for the
+            // records of tile t+2; wavefront 0 stores.
             const int pos_cur = pos_next;
-            int pg_cur = 0;
-            if (w == 0) {
-                pg_cur = page_of(pos_cur);            // issued now, used at the end
-                pos_next = position_of(t + 4);
-            }
+            const int pg_cur = page_of(pos_cur);
+            pos_next = position_of(t + 4);
             // Dequant first, so that the records of tile t+2 are issued at
             // the start of the iteration and have the whole compute phase of
             // tile t (and the barrier) to land.  (Running the two halves of
             // the workgroup in opposite phase order measured slower: the
             // late-issued loads of one half then held the barrier.)
-            if (t + 1 < T1) {
-                dequant((i + 1) & 1, (i + 1) & 3);
-                if (t + 2 < T1) load_raw((i + 2) & 3);   // lands during tile t
-            }
+            dequant((i + 1) & 1, (i + 1) & 3);
+            load_raw((i + 2) & 3);   // lands during tile t
             if (wave_active) compute(i & 1, i & 3);
-            if (w == 0 && t + 3 < T1) store_offs((i + 3) & 3, offset_of(pos_cur, pg_cur));
+            if (w == 0) store_offs((i + 3) & 3, offset_of(pos_cur, pg_cur));
             lds_barrier();
         }
     }
