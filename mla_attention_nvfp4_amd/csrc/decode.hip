@@ -177,12 +177,19 @@ void decode_kernel(DecodeArgs p) {
     // ---- offsets.  Loads are issued by every lane of wavefront 0 from
     // clamped (always valid) addresses and masked afterwards, so the
     // control flow stays uniform and the compiler's load counters exact.
-    auto position_of = [&](int t) -> int {
+    // The raw entry (the item itself, or the top-k index, loaded from a
+    // clamped address) is taken one iteration before it is validated, so
+    // that the index load is not waited for right after it is issued.
+    auto raw_of = [&](int t) -> int {
         const int item = t * kTile + (lane & (kTile - 1));
         const int ic = min(item, max(n_items - 1, 0));
-        const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
-        return (t < T1 && item < n_items && pos >= 0 && pos < L) ? pos : -1;   // (tiles past the split: masked)
+        return kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
     };
+    auto position_from = [&](int t, int raw) -> int {
+        const int item = t * kTile + (lane & (kTile - 1));
+        return (t < T1 && item < n_items && raw >= 0 && raw < L) ? raw : -1;   // (tiles past the split: masked)
+    };
+    auto position_of = [&](int t) -> int { return position_from(t, raw_of(t)); };
     auto page_of = [&](int pos) -> int {
         int pi, rem;
         page_divmod(pos < 0 ? 0 : pos, p.page_size, p.page_recip, pi, rem);
@@ -455,8 +462,8 @@ void decode_kernel(DecodeArgs p) {
         __syncthreads();
         load_raw(0);
         dequant(0, 0);
+        int raw_next = raw_of(T0 + 3);   // (before the records, as in the loop)
         load_raw(1);
-        int pos_next = position_of(T0 + 3);
         __syncthreads();
         for (int t = T0; t < T1; ++t) {
             const int i = t - T0;
@@ -466,9 +473,9 @@ void decode_kernel(DecodeArgs p) {
             // read record 0), so the compiler's load counters stay exact and
             // the wait for the page-table entry does not also wait for the
             // records of tile t+2; wavefront 0 stores.
-            const int pos_cur = pos_next;
+            const int pos_cur = position_from(t + 3, raw_next);
             const int pg_cur = page_of(pos_cur);
-            pos_next = position_of(t + 4);
+            raw_next = raw_of(t + 4);
             // Dequant first, so that the records of tile t+2 are issued at
             // the start of the iteration and have the whole compute phase of
             // tile t (and the barrier) to land.  (Running the two halves of

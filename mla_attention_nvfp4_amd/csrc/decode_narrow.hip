@@ -155,12 +155,18 @@ void decode_narrow_kernel(DecodeArgs p) {
     // ---- token addressing: tile j of this wavefront covers items
     // i0 + kNT*(w + kNW*j) .. +31; lane l handles item + 16 h2 + c16 of half h2.
     auto item_of = [&](int j, int h2) { return i0 + kNT * (w + kNW * j) + 16 * h2 + c16; };
-    auto position_of = [&](int j, int h2) -> int {
-        const int item = item_of(j, h2);
-        const int ic = min(item, max(n_items - 1, 0));
-        const int pos = kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
-        return (j < nmine && item < i1 && pos >= 0 && pos < L) ? pos : -1;
+    // The raw entry (the item itself, or the top-k index, loaded from a
+    // clamped address) is taken one iteration before it is validated, so
+    // that the index load is not waited for right after it is issued.
+    auto raw_of = [&](int j, int h2) -> int {
+        const int ic = min(item_of(j, h2), max(n_items - 1, 0));
+        return kSparse ? p.indices[(int64_t)b * p.topk + ic] : ic;
     };
+    auto position_from = [&](int j, int h2, int raw) -> int {
+        const int item = item_of(j, h2);
+        return (j < nmine && item < i1 && raw >= 0 && raw < L) ? raw : -1;
+    };
+    auto position_of = [&](int j, int h2) -> int { return position_from(j, h2, raw_of(j, h2)); };
     auto page_of = [&](int pos) -> int {
         int pi, rem;
         page_divmod(pos < 0 ? 0 : pos, p.page_size, p.page_recip, pi, rem);
@@ -346,7 +352,7 @@ void decode_narrow_kernel(DecodeArgs p) {
     if (nmine > 0) {
         Staged cur[2], nxt[2];
         int64_t offA[2], offB[2];
-        int posC[2];
+        int posC[2], rawD[2];
         int p0[2], p1[2], g0[2], g1[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -362,6 +368,7 @@ void decode_narrow_kernel(DecodeArgs p) {
             offA[h2] = offset_of(p0[h2], g0[h2]);
             offB[h2] = offset_of(p1[h2], g1[h2]);
             posC[h2] = position_of(2, h2);
+            rawD[h2] = raw_of(3, h2);
         }
         load(cur[0], offA[0]);
         load(cur[1], offA[1]);
@@ -370,7 +377,8 @@ void decode_narrow_kernel(DecodeArgs p) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 pgC[h2] = page_of(posC[h2]);              // tile j+2, used at the end
-                posD[h2] = position_of(j + 3, h2);
+                posD[h2] = position_from(j + 3, h2, rawD[h2]);
+                rawD[h2] = raw_of(j + 4, h2);             // tile j+4 (sparse: index load)
             }
             load(nxt[0], offB[0]);                        // tile j+1 (masked reloads past the end)
             load(nxt[1], offB[1]);
