@@ -63,3 +63,29 @@ def test_workload_records_bit_exact(n, decode_workload):
     rows = np.arange(T) if n == 0 else np.random.default_rng(n).choice(T, 1024, replace=False)
     print(f"  workload {n}: T={T}, checking {len(rows)} records", flush=True)
     _check_records(inp, cache, np.sort(rows))
+
+
+@pytest.mark.parametrize("outer", [float(np.float32(1 / 6)), 0.5])
+def test_block_scale_ties_bit_exact(outer):
+    """Block maxima at every e4m3 value and every midpoint between
+    neighbours, times 6 * outer (exact in bf16 for these two outer scales),
+    and their bf16 neighbours: t = amax / (6 outer) lands on the e4m3
+    rounding ties, which the kernel resolves by the exact division."""
+    from oracle import formats as F
+    inp = workloads.small_decode(31, 2, 16, [200, 100], page_size=16, rec=432, outer=outer)
+    vals = np.sort(np.unique(F.e4m3_value(np.arange(1, 0x7F)).astype(np.float64)))
+    targets = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2]) * (6.0 * np.float32(outer))
+    tb = torch.from_numpy(targets.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(tb.float().numpy().astype(np.float64), targets.astype(np.float32).astype(np.float64))
+    tbits = tb.view(torch.int16).numpy().view(np.uint16).astype(np.int64)
+    allbits = np.concatenate([tbits, tbits + 1, tbits - 1]).astype(np.uint16)
+    amax = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    T = inp.kv_c.shape[0]
+    nb = T * 32
+    rng = np.random.default_rng(5)
+    a = np.resize(amax, nb).astype(np.float32)
+    blocks = (rng.uniform(-1, 1, (nb, 16)) * a[:, None]).astype(np.float32)
+    blocks[:, 0] = np.where(rng.uniform(size=nb) < 0.5, a, -a)
+    inp.kv_c = torch.from_numpy(blocks.reshape(T, 512)).to(torch.bfloat16)
+    cache = gpu_cache(inp, fill=0xAB)
+    _check_records(inp, cache, np.arange(T))
