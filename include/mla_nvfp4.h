@@ -226,7 +226,9 @@ int mla_lse_merge(const float* partial_out, const float* partial_lse,
  *
  *  q, k         bf16 [T, H, 192], strides (q_stride_t, q_stride_h) and
  *               (k_stride_t, k_stride_h), multiples of 8, 16-byte aligned
- *  v            bf16 [T, H, 128], strides (v_stride_t, v_stride_h), same rule
+ *  v            bf16 [T, H, 128], strides (v_stride_t, v_stride_h), same rule;
+ *               q, k and v hold finite values (non-finite inputs give
+ *               unspecified outputs)
  *  cu_seqlens   int32 [N + 1], non-decreasing, cu[0] = 0, cu[N] = T
  *  max_seqlen   >= every sequence length
  *  g_*          finite, > 0 (ignored when the flag is off)

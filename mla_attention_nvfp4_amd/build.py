@@ -33,7 +33,11 @@ CFLAGS = [
 # (rare) softmax rescale of the output accumulators needs no AGPR round trip
 # and the loop-carried accumulators are not copied between register files.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "decode_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "decode_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # prefill: inputs are finite, so the max reductions of the softmax and
+         # the P blocks need no NaN canonicalization (about 12% of the
+         # attention loop's VALU instructions)
+         "prefill.hip": ["-fno-honor-nans"]}
 
 
 def sources():
