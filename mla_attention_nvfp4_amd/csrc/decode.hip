@@ -74,13 +74,13 @@ __device__ __forceinline__ f32x4 mfma_k32_f16(f16x8 a, f16x8 b, f32x4 c) {
 
 // Q k-steps kept in LDS (B-operand layout, 16 B per lane) instead of
 // registers: the RoPE part and the first kQLdsLatent latent k-steps.
-constexpr int kQLdsLatent = 8;
+constexpr int kQLdsLatent = 6;
 constexpr int kQLds = kQLdsLatent + 2;
 
 template <int NW>
 struct DecodeSmem {
     uint16_t ks[2][kTile * kKsPitch];     // 2 x 37888 B
-    u32x4 qs[NW][kQLds][64];              // NW x 6 KB
+    u32x4 qs[NW][kQLds][64];              // NW x 8 KB
     int64_t offs[kRing][kTile];           // record byte offset (masked tokens: 0, see valid)
     uint32_t valid[kRing];                // bit i: token i of the tile is unmasked
     alignas(16) uint32_t wide[kRing][NW];  // wavefront w's records of the tile exceed the single-pass bound
