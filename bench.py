@@ -192,6 +192,21 @@ def bench_cache_write(inp, steps: int, warmup: int) -> dict:
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": nbytes}
 
 
+def bench_lse_merge(steps: int, warmup: int) -> dict:
+    """mla_lse_merge on the dense decode shape: B=64 sequences, 4 splits, 128
+    heads, 512-d fp32 partials (the stand-alone merge entry point)."""
+    B, S, H, D = 64, 4, 128, 512
+    g = torch.Generator().manual_seed(4321)
+    po = torch.randn((B, S, H, D), generator=g).cuda()
+    pl = (torch.randn((B, S, H), generator=g) * 3).cuda()
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: ops.lse_merge(po, pl, out=out, lse=lse), steps, warmup)
+    nbytes = B * S * H * (D + 1) * 4 + B * H * (D + 1) * 4
+    return {"kernel_us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": nbytes}
+
+
 def bench_prefill(steps: int, warmup: int) -> dict:
     """Varlen causal prefill, 8 sequences of 2k-8k tokens, 128 heads, all four
     operand quantizers, NVFP4 output with swizzled scales and LSE."""
@@ -328,6 +343,9 @@ def main():
                                   "frac_mfma": f3 / (k3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                   "queries_per_s": inp3.B / (k3 * 1e-3), "valid_indices": nvalid}
         del b3, inp3
+        torch.cuda.empty_cache()
+        log("stand-alone LSE merge (B=64, 4 splits, 128 heads, fp32 partials)")
+        paths["lse_merge"] = bench_lse_merge(max(10, args.steps // 2), 3)
         torch.cuda.empty_cache()
         log("cache write of the decode workload's 262,144 tokens")
         paths["cache_write"] = bench_cache_write(inp, max(10, args.steps // 2), 3)

@@ -639,7 +639,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
     if (lane == 0) p.lse[(int64_t)b * p.H + h] = M + logf(wsum);
 }
 
-// One wavefront merges one (b, h).
+// One wavefront merges one (b, h).  Up to 64 splits, lane s reads split
+// s's LSE once and the weights come from wavefront reductions; the partial
+// rows are then read four splits at a time, added in split order.  More
+// splits take a plain loop over the splits.
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -648,29 +651,60 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     int n = a.splits_per_seq ? a.splits_per_seq[b] : a.S;
     n = n < 0 ? 0 : (n > a.S ? a.S : n);
     const int64_t base = (int64_t)b * a.S * a.H + h;  // row of split s: base + s*H
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_lse[base + (int64_t)s * a.H]);
     float* out = a.out + ((int64_t)b * a.H + h) * a.D;
+    float M, wsum;
+    if (n <= 64) {
+        const float l = lane < n ? a.part_lse[base + (int64_t)lane * a.H] : -INFINITY;
+        M = wave_max64(l);
+        const float wl = (l == -INFINITY || M == -INFINITY) ? 0.0f : expf(l - M);
+        wsum = wave_sum64(wl);
+        if (M != -INFINITY) {
+            const float inv = 1.0f / wsum;
+            for (int c = 4 * lane; c < a.D; c += 256) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int s0 = 0; s0 < n; s0 += 4) {
+                    f32x4 x[4];
+                    float wg[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool in = s0 + j < n;
+                        const int sj = in ? s0 + j : s0;   // (uniform)
+                        wg[j] = __int_as_float(in ? __builtin_amdgcn_readlane(__float_as_int(wl), sj) : 0);
+                        x[j] = *reinterpret_cast<const f32x4*>(a.part_out + (base + (int64_t)sj * a.H) * a.D + c);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (wg[j] != 0.0f) acc += wg[j] * x[j];   // (uniform) splits without tokens add nothing
+                }
+                *reinterpret_cast<f32x4*>(out + c) = acc * inv;
+            }
+        }
+    } else {
+        M = -INFINITY;
+        for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_lse[base + (int64_t)s * a.H]);
+        wsum = 0.0f;
+        for (int s = 0; s < n; ++s) {
+            const float l = a.part_lse[base + (int64_t)s * a.H];
+            wsum += (l == -INFINITY || M == -INFINITY) ? 0.0f : expf(l - M);
+        }
+        if (M != -INFINITY) {
+            const float inv = 1.0f / wsum;
+            for (int c = 4 * lane; c < a.D; c += 256) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < n; ++s) {
+                    const float l = a.part_lse[base + (int64_t)s * a.H];
+                    if (l == -INFINITY) continue;
+                    const float wgt = expf(l - M);
+                    acc += wgt * *reinterpret_cast<const f32x4*>(a.part_out + (base + (int64_t)s * a.H) * a.D + c);
+                }
+                *reinterpret_cast<f32x4*>(out + c) = acc * inv;
+            }
+        }
+    }
     if (M == -INFINITY) {
         for (int c = 4 * lane; c < a.D; c += 256) *reinterpret_cast<f32x4*>(out + c) = f32x4{0.f, 0.f, 0.f, 0.f};
         if (a.lse && lane == 0) a.lse[(int64_t)b * a.H + h] = -INFINITY;
         return;
-    }
-    float wsum = 0.0f;
-    for (int s = 0; s < n; ++s) {
-        const float l = a.part_lse[base + (int64_t)s * a.H];
-        wsum += (l == -INFINITY) ? 0.0f : expf(l - M);
-    }
-    const float inv = 1.0f / wsum;
-    for (int c = 4 * lane; c < a.D; c += 256) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < n; ++s) {
-            const float l = a.part_lse[base + (int64_t)s * a.H];
-            if (l == -INFINITY) continue;
-            const float wgt = expf(l - M);
-            acc += wgt * *reinterpret_cast<const f32x4*>(a.part_out + (base + (int64_t)s * a.H) * a.D + c);
-        }
-        *reinterpret_cast<f32x4*>(out + c) = acc * inv;
     }
     if (a.lse && lane == 0) a.lse[(int64_t)b * a.H + h] = M + logf(wsum);
 }

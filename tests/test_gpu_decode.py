@@ -196,6 +196,32 @@ def test_lse_merge_kernel():
     assert np.allclose(out.cpu().numpy()[3], ro, rtol=1e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("B,S,H,D", [(4, 1, 3, 4), (3, 64, 5, 100), (3, 70, 5, 100), (2, 17, 9, 4096)])
+def test_lse_merge_shapes(B, S, H, D):
+    """Split counts at and past one wavefront's lanes (64), a single split,
+    the smallest and largest rows, ragged per-sequence counts, empty splits."""
+    rng = np.random.default_rng(B * 1000 + S * 10 + D)
+    po = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    pl = (rng.standard_normal((B, S, H)) * 4).astype(np.float32)
+    pl[rng.uniform(size=(B, S, H)) < 0.2] = -np.inf
+    counts = rng.integers(0, S + 1, B).astype(np.int32)
+    counts[0] = S
+    out, lse = ops.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                             torch.from_numpy(counts).cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    for b in range(B):
+        n = counts[b]
+        if n == 0:
+            ro, rl = np.zeros((H, D)), np.full(H, -np.inf)
+        else:
+            ro, rl = OD.lse_merge(po[b, :n], pl[b, :n])
+        assert np.array_equal(np.isneginf(lse[b]), np.isneginf(rl))
+        fin = ~np.isneginf(rl)
+        assert np.allclose(out[b], ro, rtol=1e-5, atol=1e-6)
+        assert np.allclose(lse[b][fin], rl[fin], rtol=0, atol=1e-5)
+
+
 FULL = [(0, None), (1, None), (1, 16), (2, None), (3, None)]
 
 
