@@ -13,13 +13,15 @@ Printed: one JSON line with queries/s (B / step time, host clock), the
 roofline of the decode call (a second timed region of back-to-back decode
 calls between one pair of HIP events on the launch stream),
 the oracle's CPU throughput on a bounded sample, and extra lines for the
-other paths (16-head decode, top-k sparse decode, prefill).
+other paths (16-head decode, ragged decode at 128 and 16 heads, top-k
+sparse decode, the stand-alone LSE merge, the full cache write, prefill).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -332,6 +334,25 @@ def main():
                                "queries_per_s": inp16.B / (k16 * 1e-3)}
         del b16, inp16
         torch.cuda.empty_cache()
+        # Ragged decode: 128 sequences of 1k-32k tokens (2.2 M in all), e4m3
+        # RoPE (368-byte records), 1% latent outliers x20, per-sequence split
+        # counts; the cache (812 MB) is rotated over 2 copies.  The 16-head
+        # case takes the first 16 heads of the same queries.
+        log("ragged decode (workload 2: B=128, L in [1k, 32k]), 128 and 16 heads")
+        inp2 = workloads.decode_workload(2)
+        n2 = int(inp2.seq_lens.sum())
+        for H2, key in ((128, "ragged_decode"), (16, "ragged_decode_H16")):
+            inpx = inp2 if H2 == inp2.H else dataclasses.replace(inp2, H=H2, q=inp2.q[:, :H2].contiguous())
+            bx = DecodeBench(inpx, 2)
+            _, kx = bx.run(max(10, args.steps // 2), 3, with_write=False)
+            fx, byx = decode_flops(n2, H2), decode_bytes(inpx, n2, H2)
+            paths[key] = {"kernel_us": kx * 1e3, "tokens": n2,
+                          "tflops": fx / (kx * 1e-3) / 1e12, "frac_mfma": fx / (kx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "gbps": byx / (kx * 1e-3) / 1e9, "frac_hbm": byx / (kx * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "queries_per_s": inpx.B / (kx * 1e-3)}
+            del bx, inpx
+            torch.cuda.empty_cache()
+        del inp2
         log("sparse top-k decode (workload 3)")
         inp3 = workloads.decode_workload(3)
         b3 = DecodeBench(inp3, 12, sparse=True)

@@ -222,7 +222,7 @@ def test_lse_merge_shapes(B, S, H, D):
         assert np.allclose(lse[b][fin], rl[fin], rtol=0, atol=1e-5)
 
 
-FULL = [(0, None), (1, None), (1, 16), (2, None), (3, None)]
+FULL = [(0, None), (1, None), (1, 16), (2, None), (2, 16), (3, None)]
 
 
 @pytest.mark.parametrize("n,H", FULL, ids=[f"workload{n}" + (f"-H{H}" if H else "") for n, H in FULL])
