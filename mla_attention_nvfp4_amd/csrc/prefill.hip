@@ -10,9 +10,11 @@
 // layout with an fp32 global scale, replacing a separate quantization pass.
 //
 // Kernels:
-//   qk_qdq_kernel   Q and K, one thread per 16-element block along d: the
-//                   exact bf16 value s*v of every element (the tensor-wide
-//                   multiplier g is applied later, in fp32);
+//   qk_qdq_kernel   K, one thread per 16-element block along d: the exact
+//                   bf16 value s*v of every element (the tensor-wide
+//                   multiplier g is applied later, in fp32).  Q takes the
+//                   same steps inside attn_kernel, on the rows it loads
+//                   (each Q row is read by one workgroup only);
 //   v_qdq_kernel    V, one thread per (16-token block of a sequence, head,
 //                   dim): blocks start at the sequence start, the last one
 //                   may be short;
@@ -20,9 +22,9 @@
 //                   8 wavefronts x 32 rows.  Keys are visited in tiles of 64
 //                   from key 0 (the P-quantization schedule), K/V tiles
 //                   staged in registers one tile ahead and stored token-major
-//                   in LDS; S^T = K Q^T on v_mfma_f32_16x16x32_bf16; running
+//                   in LDS; S^T = K Q^T on v_mfma_f32_32x32x16_bf16; running
 //                   max refreshed per tile; P quantized in 16-key blocks
-//                   against it (exact in bf16); O^T = V^T P^T with V^T read
+//                   against it (exact in fp16); O^T = V^T P^T with V^T read
 //                   by ds_read_b64_tr_b16; epilogue: O = acc * g_p g_v / l,
 //                   NVFP4 codes and swizzled scales, LSE = m + ln l;
 //   pad_scales_kernel  zero scale bytes of the padding rows of the last
@@ -153,7 +155,9 @@ __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__
 // ----------------------------------------------------------- attention --
 
 struct AttnParams {
-    const uint16_t* q; int64_t q_st, q_sh;   // Q operand (exact bf16 s*v, or raw)
+    const uint16_t* q; int64_t q_st, q_sh;   // raw Q
+    int q_qdq;                // Q quantize-dequantized on load (multiplier q_g)
+    float q_g;
     const uint16_t* k; int64_t k_st, k_sh;
     const uint16_t* v; int64_t v_st, v_sh;
     const int32_t* cu;
@@ -252,6 +256,33 @@ void attn_kernel(AttnParams p) {
         const uint16_t* src = p.q + (int64_t)(a + rr) * p.q_st + (int64_t)h * p.q_sh + 8 * g2;
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * kk));
+    }
+    // Q quantize-dequantize, the same steps as qk_qdq_kernel: block kk of
+    // the row is this lane's 8 values and those of lane ^ 32
+    if (p.q_qdq) {
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) {
+            const u32x4 w4 = __builtin_bit_cast(u32x4, qf[kk]);
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_lo(w4[i]);
+                v[2 * i + 1] = bf16_hi(w4[i]);
+            }
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(v[i]));
+            am = xor32_max(am);
+            const Nvfp4Scale sc = nvfp4_block_scale(am, p.q_g);
+            const float scv = e4m3_decode(sc.code);
+            u32x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x2 d = e2m1_pair<0>(e2m1_pack2<0>(0u, v[2 * i] * sc.inv, v[2 * i + 1] * sc.inv));
+                o4[i] = pack_bf16_exact(d[0] * scv, d[1] * scv);
+            }
+            qf[kk] = as_bf16x8(o4);
+        }
     }
 
     // last key tile this workgroup needs; a wavefront needs tiles up to its last row
@@ -553,7 +584,6 @@ __global__ __launch_bounds__(256) void pad_scales_kernel(uint8_t* scales, int64_
 size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags) {
     size_t b = 0;
     const size_t rows = (size_t)T * H;
-    if (flags & 1u) b += rows * kDqk * 2;
     if (flags & 2u) b += rows * kDqk * 2;
     if (flags & 8u) b += rows * kDv * 2;
     return b;
@@ -569,12 +599,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.v = a.v; p.v_st = a.v_st; p.v_sh = a.v_sh;
     float gq = 1.0f, gk = 1.0f, gv = 1.0f, gp = 1.0f;
     const int64_t nqk_blocks = T * H * (kDqk / 16);
-    if (a.flags & 1u) {
-        hipLaunchKernelGGL(qk_qdq_kernel, dim3((unsigned)((nqk_blocks + 255) / 256)), dim3(256), 0, stream, a.q,
-                           a.q_st, a.q_sh, T, H, a.g_q, ws);
-        p.q = ws; p.q_st = (int64_t)H * kDqk; p.q_sh = kDqk;
+    if (a.flags & 1u) {   // (in attn_kernel)
+        p.q_qdq = 1;
+        p.q_g = a.g_q;
         gq = a.g_q;
-        ws += (size_t)T * H * kDqk;
     }
     if (a.flags & 2u) {
         hipLaunchKernelGGL(qk_qdq_kernel, dim3((unsigned)((nqk_blocks + 255) / 256)), dim3(256), 0, stream, a.k,
