@@ -114,7 +114,7 @@ def decode_workload(n: int, H: int | None = None) -> DecodeInputs:
         lens = [4096] * B
         outer = float(torch.empty(()).uniform_(0.5, 2.0, generator=g))
     elif n == 2:
-        B, Hd, shuffle, rec, splits = 128, 128, True, 368, 32
+        B, Hd, shuffle, rec, splits = 128, 128, True, 368, 8
         lens = torch.randint(1024, 32768 + 1, (B,), generator=g).tolist()
         outer = float(torch.empty(()).uniform_(0.5, 2.0, generator=g))
     elif n == 3:
