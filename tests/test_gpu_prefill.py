@@ -220,6 +220,9 @@ SMALL = [
     (4, [129, 250], 2, 11),   # Q, K, V only
     (5, [190, 64], 2, 4),     # P only
     (6, [513], 1, 15),
+    (7, [100, 33, 260], 2, 1),   # Q only (quantized as the attention kernel loads it)
+    (8, [150, 70], 2, 2),        # K only
+    (9, [90, 300], 2, 12),       # P and V (fp16 PV products, Q and K raw)
 ]
 
 
