@@ -25,8 +25,12 @@
 //                   in LDS; S^T = K Q^T on v_mfma_f32_32x32x16_bf16; running
 //                   max refreshed per tile; P quantized in 16-key blocks
 //                   against it (exact in fp16); O^T = V^T P^T with V^T read
-//                   by ds_read_b64_tr_b16; epilogue: O = acc * g_p g_v / l,
-//                   NVFP4 codes and swizzled scales, LSE = m + ln l;
+//                   by ds_read_b64_tr_b16 (with P and V quantized, the
+//                   wavefronts 4-7 run the PV products of a tile one
+//                   iteration late, next to the softmax of wavefronts 0-3 on
+//                   the same SIMDs; V tiles are triple-buffered for that);
+//                   epilogue: O = acc * g_p g_v / l, NVFP4 codes and
+//                   swizzled scales, LSE = m + ln l;
 //   pad_scales_kernel  zero scale bytes of the padding rows of the last
 //                   128-row scale tile.
 #include "device_common.hpp"
@@ -176,7 +180,7 @@ struct AttnParams {
 
 struct AttnSmem {
     uint16_t kt[2][kBN * kPitchK];  // 2 x 25600 B
-    uint16_t vt[2][kBN * kPitchV];  // 2 x 20480 B
+    uint16_t vt[3][kBN * kPitchV];  // 3 x 20480 B
     float pinv[256];                // P block scale code -> fp32(1 / fp32(e4m3(code) g_p)), 0 for d = 0
 };
 
@@ -306,7 +310,7 @@ void attn_kernel(AttnParams p) {
             sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(a + j) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15));
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int vbuf) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             const int c = tid + 512 * i;
@@ -315,7 +319,7 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 512 * i;
-            *reinterpret_cast<u32x4*>(&sm.vt[buf][(c >> 4) * kPitchV + 8 * (c & 15)]) = sv[i];
+            *reinterpret_cast<u32x4*>(&sm.vt[vbuf][(c >> 4) * kPitchV + 8 * (c & 15)]) = sv[i];
         }
     };
 
@@ -325,10 +329,39 @@ void attn_kernel(AttnParams p) {
     float m_run = -INFINITY, l_run = 0.0f;
     const float c_log2 = p.score_scale_log2;
 
-    auto compute = [&](int kt, int buf, auto mask_tag) {
+    // P of the current tile, quantized (fp16 B operand of the PV products);
+    // wavefronts 4-7 keep it for one iteration when the PV is deferred
+    f16x8 hold[4];
+    auto pv_f16 = [&](const uint16_t* vb, const f16x8 (&pp)[4]) {
+        const int s16 = lane & 15;
+        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+        auto vfrag = [&](int kb, int dt) {
+            const uint16_t* a0 = vbase + 16 * kb * kPitchV + 32 * dt;
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
+            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitchV)));
+            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
+            return u32x4{y1[0], y1[1], y2[0], y2[1]};
+        };
+        u32x4 vf[2][4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(0, dt);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb + 1 < 4) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(kb + 1, dt);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, vf[kb & 1][dt]), pp[kb], o[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto compute = [&](int kt, int buf, int vbuf, auto mask_tag, bool defer) {
         constexpr bool kMask = decltype(mask_tag)::value;
         const uint16_t* kb = sm.kt[buf];
-        const uint16_t* vb = sm.vt[buf];
+        const uint16_t* vb = sm.vt[vbuf];
         // ---- S^T for keys 32 mt2 .. +31
         f32x16 s[2] = {f32x16{}, f32x16{}};
         auto kfrag = [&](int kk, int mt2) {
@@ -390,7 +423,6 @@ void attn_kernel(AttnParams p) {
             for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
         }
         // ---- P operands per 16-key block kb
-        f16x8 pf[4];
         bf16x8 ph[4], pm[4], pl[4];
         if constexpr (kQuantP) {
             // block amax, then the four blocks' scales side by side (the rare
@@ -438,7 +470,7 @@ void attn_kernel(AttnParams p) {
                     const f16x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 1) * ss;
                     const f16x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 2) * ss;
                     const f16x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c8, 1.0f, 3) * ss;
-                    pf[kb] = f16x8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+                    hold[kb] = f16x8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
                 } else {
                     const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 0);
                     const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, 1.0f, 1);
@@ -472,6 +504,10 @@ void attn_kernel(AttnParams p) {
                 pl[kb] = as_bf16x8(lv);
             }
         }
+        if constexpr (kQuantP && kF16) {
+            if (!defer) pv_f16(vb, hold);
+            return;
+        }
         // ---- O^T += V^T P^T.  A fragment (dim tile dt, k-step kb): lane l
         // gets dim 32dt + l%32 and keys 16kb + 4 g2 + 0..3 (slots 0..3) and
         // 16kb + 8 + 4 g2 + 0..3 (slots 4..7) by two transposing reads; in each
@@ -502,7 +538,7 @@ void attn_kernel(AttnParams p) {
             for (int dt = 0; dt < 4; ++dt) {
                 const u32x4 va = vf[kb & 1][dt];
                 if constexpr (kF16) {
-                    o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, va), pf[kb], o[dt]);
+                    o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, va), hold[kb], o[dt]);
                 } else {
                     o[dt] = mfma32_bf16(as_bf16x8(va), ph[kb], o[dt]);
                     if constexpr (!kQuantP) {
@@ -516,19 +552,43 @@ void attn_kernel(AttnParams p) {
     };
 
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
     if (nkt > 1) load_tile(1);
     __syncthreads();
+    // With P and V quantized, wavefronts 4-7 (which share SIMDs with 0-3)
+    // run the PV products of tile kt at the start of iteration kt+1, so that
+    // they overlap the softmax of wavefronts 0-3 instead of their products.
+    // O sees the same operations in the same order.  Tile kt's K sits in
+    // K buffer kt % 2 and its V in V buffer kt % 3, so the V of a deferred
+    // tile stays resident for one more iteration.
+    const bool defer = (kQuantP && kF16) && w >= 4;
+    int held = -1;   // V buffer of the tile whose PV is deferred
+    int vbuf = 0;    // V buffer of tile kt
     for (int kt = 0; kt < nkt; ++kt) {
+        // (opaque to the compiler, so that it keeps one set of V addresses)
+        const int vnext = __builtin_amdgcn_readfirstlane(vbuf == 2 ? 0 : vbuf + 1);
+        if constexpr (kQuantP && kF16) {
+            if (held >= 0) {
+                pv_f16(sm.vt[held], hold);
+                held = -1;
+            }
+        }
         // a wavefront skips tiles that start after its last row; tiles
         // entirely at or below its first row need no causal mask
         if (wave_rows && kt * kBN <= wave_last_row) {
-            if (kt * kBN + kBN - 1 <= wr0) compute(kt, kt & 1, BoolTag<false>{});
-            else compute(kt, kt & 1, BoolTag<true>{});
+            if (kt * kBN + kBN - 1 <= wr0) compute(kt, kt & 1, vbuf, BoolTag<false>{}, defer);
+            else compute(kt, kt & 1, vbuf, BoolTag<true>{}, defer);
+            if constexpr (kQuantP && kF16) {
+                if (defer) held = vbuf;
+            }
         }
-        if (kt + 1 < nkt) store_tile((kt + 1) & 1);   // staged during compute(kt)
+        if (kt + 1 < nkt) store_tile((kt + 1) & 1, vnext);   // staged during compute(kt)
         if (kt + 2 < nkt) load_tile(kt + 2);          // lands during compute(kt+1)
         lds_barrier();
+        vbuf = vnext;
+    }
+    if constexpr (kQuantP && kF16) {
+        if (held >= 0) pv_f16(sm.vt[held], hold);
     }
 
     if (!wave_rows) return;
