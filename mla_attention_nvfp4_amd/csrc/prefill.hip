@@ -332,26 +332,33 @@ void attn_kernel(AttnParams p) {
     // P of the current tile, quantized (fp16 B operand of the PV products);
     // wavefronts 4-7 keep it for one iteration when the PV is deferred
     f16x8 hold[4];
+    // O^T += V^T P^T.  A fragment (dim tile dt, k-step kb) of the V tile at
+    // vb: lane l gets dim 32dt + l%32 and keys 16kb + 4 g2 + 0..3 (slots
+    // 0..3) and 16kb + 8 + 4 g2 + 0..3 (slots 4..7) by two transposing reads;
+    // in each 16-lane group lane s addresses key row k0 + s/4 and dims c0 +
+    // 4(s%4) .. +3, and receives the 4 keys of dim c0 + s.
+    const int s16 = lane & 15;
+    const int vlane = (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    auto vfrag = [&](const uint16_t* vb, int kb, int dt) {
+        const uint16_t* a0 = vb + vlane + 16 * kb * kPitchV + 32 * dt;
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
+        const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitchV)));
+        const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
+        return u32x4{y1[0], y1[1], y2[0], y2[1]};
+    };
+    // the quantized-P products (fp16); the fragments of k-step kb + 1 are
+    // read during k-step kb's products
     auto pv_f16 = [&](const uint16_t* vb, const f16x8 (&pp)[4]) {
-        const int s16 = lane & 15;
-        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-        auto vfrag = [&](int kb, int dt) {
-            const uint16_t* a0 = vbase + 16 * kb * kPitchV + 32 * dt;
-            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
-            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitchV)));
-            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-            return u32x4{y1[0], y1[1], y2[0], y2[1]};
-        };
         u32x4 vf[2][4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(0, dt);
+        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(vb, 0, dt);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (kb + 1 < 4) {
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(kb + 1, dt);
+                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(vb, kb + 1, dt);
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32_f16(__builtin_bit_cast(f16x8, vf[kb & 1][dt]), pp[kb], o[dt]);
@@ -508,31 +515,17 @@ void attn_kernel(AttnParams p) {
             if (!defer) pv_f16(vb, hold);
             return;
         }
-        // ---- O^T += V^T P^T.  A fragment (dim tile dt, k-step kb): lane l
-        // gets dim 32dt + l%32 and keys 16kb + 4 g2 + 0..3 (slots 0..3) and
-        // 16kb + 8 + 4 g2 + 0..3 (slots 4..7) by two transposing reads; in each
-        // 16-lane group lane s addresses key row k0 + s/4 and dims c0 + 4(s%4)
-        // .. +3, and receives the 4 keys of dim c0 + s.
-        const int s16 = lane & 15;
-        const uint16_t* vbase = vb + (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-        auto vfrag = [&](int kb, int dt) {
-            const uint16_t* a0 = vbase + 16 * kb * kPitchV + 32 * dt;
-            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0)));
-            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(a0 + 8 * kPitchV)));
-            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-            return u32x4{y1[0], y1[1], y2[0], y2[1]};
-        };
-        // the fragments of k-step kb + 1 are read during k-step kb's products
+        // ---- O^T += V^T P^T in bf16 (P unquantized as three parts, or V
+        // unquantized); the fragments of k-step kb + 1 are read during k-step
+        // kb's products
         u32x4 vf[2][4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(0, dt);
+        for (int dt = 0; dt < 4; ++dt) vf[0][dt] = vfrag(vb, 0, dt);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (kb + 1 < 4) {
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(kb + 1, dt);
+                for (int dt = 0; dt < 4; ++dt) vf[(kb + 1) & 1][dt] = vfrag(vb, kb + 1, dt);
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
