@@ -413,37 +413,36 @@ void decode_narrow_kernel(DecodeArgs p) {
     }
 #pragma unroll
     for (int c = 0; c < 32; ++c) o[c] *= aw;
-    // sum of the four O's through LDS (f32x4 per (dim tile, lane))
-    f32x4* area = reinterpret_cast<f32x4*>(&sm.vt[0][0]);   // 2 x 32 KB
-    __syncthreads();
-    if (w >= 2) {
+    // sum of the four O's through LDS: each wavefront stores its weighted O
+    // over its own V tile (f32x4 per (dim tile, lane)); then wavefront w
+    // sums dim tiles 8w .. 8w+7 of all four, as (O0 + O2) + (O1 + O3), and
+    // writes them
+    {
+        f32x4* mine = reinterpret_cast<f32x4*>(&sm.vt[w][0]);
 #pragma unroll
-        for (int c = 0; c < 32; ++c) area[(w - 2) * 2048 + c * 64 + lane] = o[c];
+        for (int c = 0; c < 32; ++c) mine[c * 64 + lane] = o[c];
     }
     __syncthreads();
-    if (w < 2) {
+    f32x4 r[8];
 #pragma unroll
-        for (int c = 0; c < 32; ++c) o[c] += area[w * 2048 + c * 64 + lane];
+    for (int k = 0; k < 8; ++k) {
+        const int c = 8 * w + k;
+        const f32x4 v0 = reinterpret_cast<const f32x4*>(&sm.vt[0][0])[c * 64 + lane];
+        const f32x4 v1 = reinterpret_cast<const f32x4*>(&sm.vt[1][0])[c * 64 + lane];
+        const f32x4 v2 = reinterpret_cast<const f32x4*>(&sm.vt[2][0])[c * 64 + lane];
+        const f32x4 v3 = reinterpret_cast<const f32x4*>(&sm.vt[3][0])[c * 64 + lane];
+        r[k] = (v0 + v2) + (v1 + v3);
     }
-    __syncthreads();
-    if (w == 1) {
-#pragma unroll
-        for (int c = 0; c < 32; ++c) area[c * 64 + lane] = o[c];
-    }
-    __syncthreads();
-    if (w != 0) return;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) o[c] += area[c * 64 + lane];
 
     const bool any = ltot > 0.0f;
     const float so = any ? outer / ltot : 0.0f;
     const float lse_v = any ? (M + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
     if (!hok) return;
-    // element i of o[c]: dim 16c + 4gq + i of head c16
+    // element i of r[k]: dim 16(8w + k) + 4gq + i of head c16
     float* dst;
     if (ns == 1) {
         dst = p.out + ((int64_t)b * p.H + c16) * kLatent;
-        if (gq == 0) p.lse[(int64_t)b * p.H + c16] = lse_v;
+        if (w == 0 && gq == 0) p.lse[(int64_t)b * p.H + c16] = lse_v;
     } else {
         // split partial: fp16 in the first half of its row when no tile of
         // the split exceeded the latent bound (|partial| <= 8, absolute
@@ -451,23 +450,23 @@ void decode_narrow_kernel(DecodeArgs p) {
         const int64_t row = ((int64_t)b * p.max_splits + s) * p.H + c16;
         const bool wide = (sm.wide[0] | sm.wide[1] | sm.wide[2] | sm.wide[3]) != 0u;
         dst = p.ws_out + row * kLatent;
-        if (gq == 0) {
+        if (w == 0 && gq == 0) {
             p.ws_lse[row] = lse_v;
             p.ws_fmt[row] = wide ? 0 : 1;
         }
         if (!wide) {
             _Float16* dh = reinterpret_cast<_Float16*>(dst);
 #pragma unroll
-            for (int c = 0; c < 32; ++c) {
-                const f32x4 v = o[c] * so;
-                *reinterpret_cast<f16x4*>(dh + 16 * c + 4 * gq) =
+            for (int k = 0; k < 8; ++k) {
+                const f32x4 v = r[k] * so;
+                *reinterpret_cast<f16x4*>(dh + 16 * (8 * w + k) + 4 * gq) =
                     f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
             }
             return;
         }
     }
 #pragma unroll
-    for (int c = 0; c < 32; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c + 4 * gq) = o[c] * so;
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<f32x4*>(dst + 16 * (8 * w + k) + 4 * gq) = r[k] * so;
 }
 
 template <bool kRopeFp8, bool kSparse>
