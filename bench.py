@@ -279,7 +279,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is measured "
-              f"on one GPU's share, see the sharding notes in DESIGN.md", flush=True)
+              f"on one GPU's share", flush=True)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", flush=True)
