@@ -13,7 +13,7 @@ Printed: one JSON line with queries/s (B / step time, host clock), the
 roofline of the decode call (a second timed region of back-to-back decode
 calls between one pair of HIP events on the launch stream),
 the oracle's CPU throughput on a bounded sample, and extra lines for the
-other paths (16-head decode, ragged decode at 128 and 16 heads, top-k
+other paths (tiny decode, 16-head decode, ragged decode at 128 and 16 heads, top-k
 sparse decode, the stand-alone LSE merge, the full cache write, prefill).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
@@ -324,6 +324,14 @@ def main():
 
     if not args.no_extra:
         paths = {}
+        log("tiny decode (workload 0: B=1, H=16, L=256)")
+        inp0 = workloads.decode_workload(0)
+        b0 = DecodeBench(inp0, 1)
+        _, k0 = b0.run(max(10, args.steps // 2), 5, with_write=False)
+        paths["tiny_decode"] = {"kernel_us": k0 * 1e3, "note": "launch-latency bound: one decode call, "
+                                "back-to-back calls between one event pair"}
+        del b0, inp0
+        torch.cuda.empty_cache()
         log("16-head decode (workload 1 shape, H=16)")
         inp16 = workloads.decode_workload(1, H=16)
         b16 = DecodeBench(inp16, ROTATE)
