@@ -360,6 +360,9 @@ def main():
                           "queries_per_s": inpx.B / (kx * 1e-3)}
             del bx, inpx
             torch.cuda.empty_cache()
+        log("cache write of the ragged workload's 2.2 M tokens (368-byte records, e4m3 RoPE)")
+        paths["cache_write_ragged"] = bench_cache_write(inp2, max(10, args.steps // 2), 3)
+        torch.cuda.empty_cache()
         del inp2
         log("sparse top-k decode (workload 3)")
         inp3 = workloads.decode_workload(3)

@@ -82,9 +82,7 @@ void cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_stride,
         // RoPE: two values per lane
         if (lane < 32) {
             if (kRopeFp8) {
-                const uint32_t c0 = e4m3_encode(bf16_lo(pe[j]));
-                const uint32_t c1 = e4m3_encode(bf16_hi(pe[j]));
-                reinterpret_cast<uint16_t*>(rec + 288)[lane] = (uint16_t)(c0 | (c1 << 8));
+                reinterpret_cast<uint16_t*>(rec + 288)[lane] = (uint16_t)e4m3_encode2_hw(bf16_lo(pe[j]), bf16_hi(pe[j]));
             } else {
                 reinterpret_cast<uint32_t*>(rec + 288)[lane] = pe[j];
             }

@@ -50,6 +50,16 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float t) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xffu;
 }
 
+// e4m3 codes of two signed values by one FP8 conversion, in bytes 0 and 1:
+// the sign bit over the code of min(|t|, 448) (as e4m3_encode_nonneg), which
+// is e4m3_encode's code for every fp32 input, +-inf and NaN included (they
+// saturate to 0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode2_hw(float t0, float t1) {
+    const uint32_t mag = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(__builtin_fabsf(t0), 448.0f),
+                                                                   fminf(__builtin_fabsf(t1), 448.0f), 0, false) & 0xffffu;
+    return mag | ((f2u(t0) >> 24) & 0x80u) | ((f2u(t1) >> 16) & 0x8000u);
+}
+
 // fp32 value of an e4m3 code by the gfx950 FP8 conversion (OCP E4M3FN,
 // exact; codes 0x7F/0xFF are NaN and never produced by the encoders here).
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {

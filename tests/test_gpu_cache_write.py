@@ -89,3 +89,24 @@ def test_block_scale_ties_bit_exact(outer):
     inp.kv_c = torch.from_numpy(blocks.reshape(T, 512)).to(torch.bfloat16)
     cache = gpu_cache(inp, fill=0xAB)
     _check_records(inp, cache, np.arange(T))
+
+
+def test_fp8_rope_every_finite_bf16_value():
+    """The e4m3 RoPE cast over every finite bf16 bit pattern (both signs,
+    subnormal e4m3 range, ties, values far above 448), bit-exact."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (pats & 0x7F80) != 0x7F80
+    pats = pats[finite]
+    T = (pats.size + 63) // 64
+    pe = np.zeros(T * 64, dtype=np.uint16)
+    pe[:pats.size] = pats
+    g = torch.Generator().manual_seed(55)
+    kv = torch.randn((T, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.from_numpy(pe.view(np.int16).reshape(T, 64).copy()).view(torch.bfloat16)
+    slots = torch.arange(T, dtype=torch.int64)
+    cache = torch.full((T, 368), 0xAB, dtype=torch.uint8, device="cuda")
+    ops.cache_write(kv.cuda(), k_pe.cuda(), slots.cuda(), cache, 1.0)
+    got = cache.cpu().numpy()
+    want = OR.pack_records(bits(kv), bits(k_pe), 1.0, 368)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at (row, byte) {bad[:5].tolist()}"
