@@ -61,7 +61,7 @@ typedef enum {
 #define MLA_PREFILL_D_QK 192
 #define MLA_PREFILL_D_V 128
 /* Key-tile width of the prefill P-quantization schedule (see
- * mla_prefill_nvfp4_out). */
+ * mla_prefill_nvfp4_out); mla_prefill_p_tile() returns the library's value. */
 #define MLA_PREFILL_P_TILE 64
 /* Decode splits cover at least this many tokens (see mla_decode_num_splits). */
 #define MLA_DECODE_MIN_SPLIT_TOKENS 256
@@ -95,6 +95,15 @@ int mla_decode_num_splits(int seq_len, int max_splits);
  * region 256-byte aligned.  0 when max_splits <= 1.  No initial contents are
  * needed; calls that may run concurrently need separate workspaces. */
 size_t mla_decode_workspace_bytes(int B, int H, int max_splits);
+
+/* Key-tile width BN_P of the prefill's P-quantization schedule: keys are
+ * visited in tiles of BN_P from key 0, and P is quantized against the running
+ * max as it stands after each tile.  [MO-MLA], commit 1: its eager oracles
+ * follow the kernels' schedules, because P's quantization depends on the max
+ * the kernel holds when it quantizes; the tile width is therefore part of the
+ * definition of mla_prefill_nvfp4_out with MLA_QDQ_P set.  Returns the value
+ * the kernels were compiled with (MLA_PREFILL_P_TILE). */
+int mla_prefill_p_tile(void);
 
 /* Bytes of a 128x4-swizzled e4m3 scale buffer for `rows` rows of
  * `scale_cols` scales: ceil(rows/128)*128 * (ceil(scale_cols/4)*4). */
@@ -190,7 +199,7 @@ int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
                             float* out, float* lse, void* stream);
 
 /* Merge S partial attention results over disjoint token sets.  [MO-MLA],
- * commit 1: natural-log LSE "for chunked-context merging".  For each (b, h)
+ * commit 1: partials carry a natural-log LSE so that chunks can be merged.  For each (b, h)
  * with n = splits_per_seq[b] (clamped to [0, S]; all S when the pointer is
  * NULL): M = max_{s<n} lse_s; if n == 0 or M == -inf, out = 0 and lse = -inf;
  * else w_s = e^(lse_s - M), out = sum w_s out_s / sum w_s, lse = M + ln sum w_s.

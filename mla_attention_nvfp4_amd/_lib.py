@@ -23,6 +23,7 @@ SIGNATURES = {
     "mla_nvfp4_record_bytes": (c_int, [c_int]),
     "mla_decode_num_splits": (c_int, [c_int, c_int]),
     "mla_decode_workspace_bytes": (c_sz, [c_int, c_int, c_int]),
+    "mla_prefill_p_tile": (c_int, []),
     "mla_nvfp4_swizzled_scale_bytes": (c_sz, [c_i64, c_i64]),
     "mla_nvfp4_cache_write": (c_int, [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_int, c_f32, c_p]),
     "mla_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_int,
@@ -39,7 +40,6 @@ SIGNATURES = {
 }
 
 MLA_QDQ_Q, MLA_QDQ_K, MLA_QDQ_P, MLA_QDQ_V = 1, 2, 4, 8
-PREFILL_P_TILE = 64
 
 
 class MlaError(RuntimeError):
@@ -99,6 +99,11 @@ def decode_num_splits(n: int, max_splits: int) -> int:
 
 def decode_workspace_bytes(B: int, H: int, max_splits: int) -> int:
     return lib().mla_decode_workspace_bytes(B, H, max_splits)
+
+
+def prefill_p_tile() -> int:
+    """Key-tile width of the prefill's P-quantization schedule, as compiled."""
+    return lib().mla_prefill_p_tile()
 
 
 def swizzled_scale_bytes(rows: int, scale_cols: int) -> int:

@@ -65,7 +65,7 @@ int hip_status(hipError_t e, const char* what) {
 
 int check_record(int record_bytes) {
     if (record_bytes != MLA_RECORD_BYTES_BF16_ROPE && record_bytes != MLA_RECORD_BYTES_FP8_ROPE)
-        return fail(MLA_ERR_RECORD_BYTES, "NVFP4 MLA cache record must be 368 or 432 bytes, got %d",
+        return fail(MLA_ERR_RECORD_BYTES, "record_bytes=%d is neither the bf16-RoPE width (432) nor the e4m3-RoPE width (368)",
                     record_bytes);
     return MLA_OK;
 }
@@ -150,6 +150,8 @@ size_t mla_decode_workspace_bytes(int B, int H, int max_splits) {
     return decode_ws_out_bytes(B, H, max_splits) + decode_ws_lse_bytes(B, H, max_splits) +
            decode_ws_fmt_bytes(B, H, max_splits);
 }
+
+int mla_prefill_p_tile(void) { return mla::prefill_p_tile(); }
 
 size_t mla_nvfp4_swizzled_scale_bytes(int64_t rows, int64_t scale_cols) {
     if (rows <= 0 || scale_cols <= 0) return 0;

@@ -127,6 +127,29 @@ __device__ __forceinline__ Nvfp4Scale nvfp4_block_scale(float a, float g) {
     return Nvfp4Scale{s, (d == 0.0f) ? 0.0f : 1.0f / d};
 }
 
+// The scale quotient t = fp32(a / u) taken as one multiply by
+// inv_u = fp32(1 / u): the product lies within two ulps of the correctly
+// rounded quotient, so its e4m3 code can differ only where it is within a few
+// ulps of an e4m3 rounding tie (the 20 mantissa bits below the kept 3 near
+// one half) or in the subnormal range (below 2^-6, where the rounding is done
+// on t * 512).  Such values must redo the exact division.
+__device__ __forceinline__ bool scale_quotient_near_tie(float tq) {
+    const uint32_t rem = f2u(tq) & 0xfffffu;
+    return tq < 0.015625f || (rem > 0x80000u - 8u && rem < 0x80000u + 8u);
+}
+
+// nvfp4_block_scale with the quotient by multiplication: u = fp32(6 g) and
+// inv_u = fp32(1 / u) are given; the exact division is redone only where
+// scale_quotient_near_tie says the code could differ, so the scale code and
+// inv are those of nvfp4_block_scale.
+__device__ __forceinline__ Nvfp4Scale nvfp4_block_scale_fast(float a, float g, float u, float inv_u) {
+    float t = a * inv_u;
+    if (scale_quotient_near_tie(t)) t = a / u;
+    const uint32_t s = e4m3_encode_nonneg(t);
+    const float d = e4m3_decode(s) * g;
+    return Nvfp4Scale{s, (d == 0.0f) ? 0.0f : 1.0f / d};
+}
+
 // Byte offset of scale (m, c) in the 128x4-swizzled layout with cpad
 // (a multiple of 4) scale columns: tiles of 128 rows x 4 columns (512 B),
 // row-tile major; inside a tile (m % 32) * 16 + ((m % 128) / 32) * 4 + c % 4.

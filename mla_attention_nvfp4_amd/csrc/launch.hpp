@@ -73,6 +73,7 @@ struct PrefillArgs {
 };
 
 size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags);
+int prefill_p_tile();   // the attention kernel's key tile (the P schedule)
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Division of a token position by the page size without an integer

@@ -184,16 +184,10 @@ struct AttnSmem {
     float pinv[256];                // P block scale code -> fp32(1 / fp32(e4m3(code) g_p)), 0 for d = 0
 };
 
-// The P block scale's t = fp32(a / u) is taken as one multiply with
-// fp32(1/u): the product lies within two ulps of the quotient, so its e4m3
-// code can differ only when it is within a few ulps of an e4m3 rounding tie
-// (mantissa bits below the kept 3 near one half) or in the subnormal range,
-// where the rounding is done on t * 512.  Such values redo the exact
-// division.
-__device__ __forceinline__ bool p_scale_near(float tq) {
-    const uint32_t rem = f2u(tq) & 0xfffffu;
-    return tq < 0.015625f || (rem > 0x80000u - 8u && rem < 0x80000u + 8u);
-}
+// The P block scale's quotient t = fp32(a / u) is taken as one multiply by
+// fp32(1/u), redone as the exact division where scale_quotient_near_tie says
+// the code could differ (as nvfp4_block_scale_fast, which the row quantizer
+// uses; its tests sweep the e4m3 ties with u not a power of two).
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -448,7 +442,7 @@ void attn_kernel(AttnParams p) {
             for (int kb = 0; kb < 4; ++kb) {
                 am[kb] = xor32_max(am[kb]);
                 tq[kb] = am[kb] * p.inv_u_p;
-                nr[kb] = p_scale_near(tq[kb]);
+                nr[kb] = scale_quotient_near_tie(tq[kb]);
                 any_near |= nr[kb];
             }
             if (__any(any_near)) {
@@ -633,6 +627,8 @@ __global__ __launch_bounds__(256) void pad_scales_kernel(uint8_t* scales, int64_
 }
 
 }  // namespace
+
+int prefill_p_tile() { return kBN; }
 
 size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags) {
     size_t b = 0;

@@ -14,9 +14,9 @@ head h, each cached token j < L contributes
                                                       [MO-MLA], commit 3)
 
     out = sum_j e^(z_j - m) v_j / sum_j e^(z_j - m),  m = max_j z_j
-    lse = m + ln sum_j e^(z_j - m)                   (natural log: [MO-MLA],
-                                                      commit 1, "for chunked-
-                                                      context merging")
+    lse = m + ln sum_j e^(z_j - m)                   (natural log, so that
+                                                      chunks merge: [MO-MLA],
+                                                      commit 1)
 
 Record j of sequence b sits at slot page_table[b][j // P] * P + j % P of the
 cache viewed as [slots, record_bytes].  L = 0 gives out = 0 and lse = -inf.

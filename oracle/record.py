@@ -49,7 +49,7 @@ def rope_is_fp8(rec_bytes: int) -> bool:
         return True
     if rec_bytes == RECORD_BYTES_BF16_ROPE:
         return False
-    raise ValueError(f"NVFP4 MLA cache record must be 368 or 432 bytes, got {rec_bytes}")
+    raise ValueError(f"record width {rec_bytes} is neither 432 (bf16 RoPE) nor 368 (e4m3 RoPE)")
 
 
 def pack_records(kv_c_bits, k_pe_bits, outer_scale, rec_bytes: int) -> np.ndarray:

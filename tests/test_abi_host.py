@@ -45,6 +45,11 @@ def test_constants_and_policy():
     assert L.swizzled_scale_bytes(129, 1024) == 256 * 1024
 
 
+def test_prefill_p_tile_is_the_oracle_schedule():
+    from oracle import prefill as OP
+    assert L.prefill_p_tile() == OP.BN_P == 64
+
+
 def _decode_args(**kw):
     a = dict(q_nope=1 << 20, q_rope=1 << 20, sb=576 * 128, sh=576, cache=1 << 20, num_pages=4,
              rec=432, page=64, pt=1 << 20, maxp=4, seq=1 << 20, B=1, H=16, outer=1.0, scale=0.04,

@@ -21,6 +21,8 @@ SMALL_DENSE = [
     (8, 3, 16, [700, 33, 2000], 16, 368, 1.4, 3),     # narrow heads, e4m3 RoPE, outliers
     (9, 2, 7, [300, 1029], 48, 432, 0.6, 2),          # narrow, 7 heads
     (10, 2, 100, [555, 1200], 64, 368, 1.1, 2),       # wide, partial head group
+    (16, 2, 256, [700, 1500], 64, 432, 1.2, 3),       # two 128-head groups
+    (17, 1, 300, [400], 16, 368, 0.9, 2),             # three head groups, the last partial
 ]
 
 
@@ -93,6 +95,7 @@ SMALL_SPARSE = [
     (12, 3, 16, [100, 5, 700], 96, 0.1, 2),
     (13, 2, 128, [5000, 3000], 512, 0.1, 4),
     (14, 2, 48, [64, 300], 130, 0.5, 3),
+    (18, 2, 256, [3000, 800], 300, 0.1, 2),           # two 128-head groups
 ]
 
 
@@ -127,29 +130,28 @@ def test_sparse_all_masked_and_masked_pages():
     compare(out, lse, ref_out, ref_lse, [1], "sparse-masked")
 
 
-def test_out_of_range_page_ids_are_masked():
-    """A page id outside the cache masks its tokens instead of being read."""
-    inp = workloads.small_decode(22, 1, 16, [192], page_size=64, rec=432)
+@pytest.mark.parametrize("H", [16, 128], ids=["narrow", "wide"])
+def test_out_of_range_page_ids_are_masked(H):
+    """A page id outside the cache masks its tokens instead of being read:
+    the result is the oracle's attention over the remaining tokens (its
+    sparse decode over every position but those of the masked page)."""
+    inp = workloads.small_decode(22, 2, H, [192, 300], page_size=64, rec=432, max_splits=2)
     cache = gpu_cache(inp)
     pt = inp.page_table.clone()
     pt[0, 1] = 10 ** 6
+    pt[1, 3] = -5
     q = inp.q.cuda()
     out, lse = ops.decode(q[..., :512], q[..., 512:], cache, pt.cuda(), inp.seq_lens.cuda(),
-                          inp.outer_scale, inp.softmax_scale, 1)
-    # reference: the same sequence without its second page
-    flat = torch.cat([cache.view(-1, 432)[inp.slot_mapping[:64].cuda()],
-                      cache.view(-1, 432)[inp.slot_mapping[128:].cuda()]]).view(2, 64, 432)
-    out2, lse2 = ops.decode(q[..., :512], q[..., 512:], flat.contiguous(),
-                            torch.tensor([[0, 1]], dtype=torch.int32, device="cuda"),
-                            torch.tensor([128], dtype=torch.int32, device="cuda"),
-                            inp.outer_scale, inp.softmax_scale, 1)
+                          inp.outer_scale, inp.softmax_scale, 2)
     torch.cuda.synchronize()
-    # The two launches cut the tokens into different tiles, so the running
-    # maximum, and with it the fp16 rounding of P, differs: the outputs agree
-    # to 2^-11 max|V| (single-pass bound), not bit for bit.
-    assert torch.isfinite(out).all()
-    assert float((out - out2).abs().max()) <= 2.0 ** -11 * 8.0
-    assert torch.allclose(lse, lse2, atol=1e-5)
+    keep = [[j for j in range(192) if j // 64 != 1], [j for j in range(300) if j // 64 != 3]]
+    idx = np.full((2, 300), -1, np.int64)
+    for b in range(2):
+        idx[b, :len(keep[b])] = keep[b]
+    inp.indices = torch.from_numpy(idx.astype(np.int32))      # the oracle's reference only
+    ref_out, ref_lse = oracle_decode(inp, [0, 1])
+    compare(out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse, [0, 1],
+            f"masked-pages-H{H}")
 
 
 def test_split_counts_agree_and_runs_are_deterministic():

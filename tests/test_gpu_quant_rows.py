@@ -69,3 +69,44 @@ def test_quantize_rows_scale_rounding_sweep():
     want_codes, want_scales = S.quantize_rows(x, g)
     assert np.array_equal(scales.cpu().numpy(), want_scales)
     assert np.array_equal(codes.cpu().numpy(), want_codes)
+
+
+def test_quantize_rows_scale_quotient_sweep():
+    """The scale quotient t = a / (6 g) is formed as a * fp32(1 / (6 g)) with
+    the division redone near e4m3 rounding ties (the P blocks of the prefill
+    form it the same way).  With g = fp32(1/2688), the P multiplier, 6g is not
+    a power of two and the product can differ from the quotient in its last
+    bits.  The block maxima here put the quotient on every e4m3 value and
+    every midpoint between neighbours, and up to 6 fp32 ulps of the maximum
+    either side, plus the subnormal range and saturation: codes and swizzled
+    scales must equal the oracle's (true division) bit for bit."""
+    from oracle import formats as F
+    g32 = np.float32(1 / 2688)
+    u = np.float32(np.float32(6) * g32)
+    vals = np.sort(np.unique(F.e4m3_value(np.arange(0, 0x7F)).astype(np.float64)))
+    ties = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2, [448.0, 464.0, 2.0 ** -10, 3 * 2.0 ** -11]])
+    a0 = (ties * np.float64(u)).astype(np.float32)
+    pts = [a0]
+    up, dn = a0.copy(), a0.copy()
+    for _ in range(6):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(0))
+        pts += [up.copy(), dn.copy()]
+    amax = np.concatenate(pts)
+    M, K = 64, (amax.size + 63) // 64 * 16
+    rng = np.random.default_rng(9)
+    amax = np.concatenate([amax, rng.uniform(0, 1.2, M * K // 16 - amax.size).astype(np.float32)])
+    frac = rng.uniform(-1, 1, (amax.size, 16)).astype(np.float32)
+    blocks = (frac * amax[:, None]).astype(np.float32)
+    blocks[:, 0] = amax
+    x = blocks.reshape(M, K)
+    # the fixture holds blocks where the plain product a * fp32(1/u) would
+    # take another scale code than the quotient: those the redo must fix
+    inv_u = np.float32(np.float32(1) / u)
+    differs = F.e4m3_encode((amax * inv_u).astype(np.float32)) != F.e4m3_encode((amax / u).astype(np.float32))
+    assert int(differs.sum()) >= 20
+    codes, scales = ops.quantize_rows(torch.from_numpy(x).cuda(), float(g32))
+    torch.cuda.synchronize()
+    want_codes, want_scales = S.quantize_rows(x, float(g32))
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
