@@ -177,6 +177,27 @@ int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
                      void* workspace, size_t workspace_bytes,
                      float* out, float* lse, void* stream);
 
+/* Allocation-free form of mla_decode_nvfp4, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as mla_decode_nvfp4
+ * without the workspace: the split partials go to a scratch array of
+ * MLA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on, from load until the process ends.  A request whose workspace
+ * (mla_decode_workspace_bytes(B, H, max_splits)) exceeds that size returns
+ * MLA_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.  The call allocates and
+ * frees nothing; the scratch needs no initial contents.  Every call on one
+ * device shares that device's scratch: calls that may overlap on one device
+ * (different streams, or other host threads) race and must be serialised by
+ * the caller. */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mla_decode_nvfp4_noalloc(const uint16_t* q_nope, const uint16_t* q_rope,
+                             int64_t q_stride_b, int64_t q_stride_h,
+                             const uint8_t* cache, int64_t num_pages, int record_bytes,
+                             int page_size, const int32_t* page_table, int max_pages_per_seq,
+                             const int32_t* seq_lens, int B, int H,
+                             float outer_scale, float softmax_scale, int max_splits,
+                             float* out, float* lse, void* stream);
+
 /* Top-k sparse decode: as mla_decode_nvfp4, but sequence b attends only to
  * the tokens listed in indices[b][0..topk).  [B12X], walkthrough and
  * sequence diagram (sparse MLA decode on the NVFP4 cache with the latent

@@ -28,6 +28,8 @@ SIGNATURES = {
     "mla_nvfp4_cache_write": (c_int, [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_int, c_f32, c_p]),
     "mla_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_int,
                                  c_int, c_f32, c_f32, c_int, c_p, c_sz, c_p, c_p, c_p]),
+    "mla_decode_nvfp4_noalloc": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p,
+                                         c_int, c_int, c_f32, c_f32, c_int, c_p, c_p, c_p]),
     "mla_sparse_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p,
                                         c_int, c_int, c_f32, c_f32, c_p, c_int, c_int, c_p, c_sz, c_p, c_p,
                                         c_p]),
@@ -173,6 +175,23 @@ def decode(q_nope, q_rope, cache, page_table, seq_lens, outer_scale, softmax_sca
         cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
         seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), int(max_splits), _ptr(ws),
         0 if ws is None else ws.numel(), out.data_ptr(), lse.data_ptr(), _stream(q_nope)))
+    return out, lse
+
+
+def decode_noalloc(q_nope, q_rope, cache, page_table, seq_lens, outer_scale, softmax_scale, max_splits=1,
+                   out=None, lse=None):
+    """Dense paged decode through the allocation-free entry point: the split
+    partials use the library's per-device scratch (no workspace argument).
+    ``out`` and ``lse`` are allocated here only when not given."""
+    _decode_common(q_nope, q_rope, cache, page_table, seq_lens)
+    B, H = q_nope.shape[:2]
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=q_nope.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device) if lse is None else lse
+    _check(lib().mla_decode_nvfp4_noalloc(
+        q_nope.data_ptr(), q_rope.data_ptr(), q_nope.stride(0), q_nope.stride(1), cache.data_ptr(),
+        cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+        seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), int(max_splits), out.data_ptr(),
+        lse.data_ptr(), _stream(q_nope)))
     return out, lse
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/mla_nvfp4.h"
@@ -131,6 +132,73 @@ int run_decode(mla::DecodeArgs& a, void* workspace, hipStream_t stream) {
     return hip_status(mla::launch_decode(a, stream), "decode launch");
 }
 
+// Scratch memory of mla_decode_nvfp4_noalloc: the decode workspace (split
+// partials) for callers that cannot allocate.  Each device holds its own copy
+// of this array from the library's load until the process ends; host code
+// uses only the per-device address from hipGetSymbolAddress (the array's name
+// is a host-side stand-in, not a device address).  Every call on a device
+// shares that device's copy.
+static __device__ __align__(256) uint8_t scratch[MLA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on device d (null until looked up)
+
+// Address of the current device's scratch array, looked up once per device
+// with that device current.
+int scratch_of_current_device(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
+int decode_entry(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b, int64_t q_stride_h,
+                 const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                 const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
+                 float outer_scale, float softmax_scale, int max_splits, void* workspace,
+                 size_t workspace_bytes, float* out, float* lse, void* stream) {
+    int rc = check_decode(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                          page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                          workspace, workspace_bytes, out, lse);
+    if (rc) return rc;
+    if (B == 0) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    mla::DecodeArgs a{};
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.q_stride_b = q_stride_b;
+    a.q_stride_h = q_stride_h;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.record_bytes = record_bytes;
+    a.page_size = page_size;
+    a.page_recip = mla::page_recip_of(page_size);
+    a.page_table = page_table;
+    a.max_pages = max_pages_per_seq;
+    a.seq_lens = seq_lens;
+    a.indices = nullptr;
+    a.topk = 0;
+    a.B = B;
+    a.H = H;
+    a.outer_scale = outer_scale;
+    a.softmax_scale = softmax_scale;
+    a.max_splits = max_splits;
+    a.out = out;
+    a.lse = lse;
+    return run_decode(a, workspace, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,36 +255,37 @@ int mla_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_s
                      const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
                      float outer_scale, float softmax_scale, int max_splits, void* workspace,
                      size_t workspace_bytes, float* out, float* lse, void* stream) {
-    int rc = check_decode(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
-                          page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
-                          workspace, workspace_bytes, out, lse);
-    if (rc) return rc;
-    if (B == 0) return ok();
-    rc = check_device();
-    if (rc) return rc;
-    mla::DecodeArgs a{};
-    a.q_nope = q_nope;
-    a.q_rope = q_rope;
-    a.q_stride_b = q_stride_b;
-    a.q_stride_h = q_stride_h;
-    a.cache = cache;
-    a.num_pages = num_pages;
-    a.record_bytes = record_bytes;
-    a.page_size = page_size;
-    a.page_recip = mla::page_recip_of(page_size);
-    a.page_table = page_table;
-    a.max_pages = max_pages_per_seq;
-    a.seq_lens = seq_lens;
-    a.indices = nullptr;
-    a.topk = 0;
-    a.B = B;
-    a.H = H;
-    a.outer_scale = outer_scale;
-    a.softmax_scale = softmax_scale;
-    a.max_splits = max_splits;
-    a.out = out;
-    a.lse = lse;
-    return run_decode(a, workspace, static_cast<hipStream_t>(stream));
+    return decode_entry(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                        page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                        workspace, workspace_bytes, out, lse, stream);
+}
+
+int mla_decode_nvfp4_noalloc(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b,
+                             int64_t q_stride_h, const uint8_t* cache, int64_t num_pages, int record_bytes,
+                             int page_size, const int32_t* page_table, int max_pages_per_seq,
+                             const int32_t* seq_lens, int B, int H, float outer_scale, float softmax_scale,
+                             int max_splits, float* out, float* lse, void* stream) {
+    // the size limit first (a pure host check), then the scratch address
+    if (B > 0 && H > 0 && max_splits > 1) {
+        const size_t need = mla_decode_workspace_bytes(B, H, max_splits);
+        if (need > (size_t)MLA_DECODE_NOALLOC_SCRATCH_BYTES)
+            return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                        "B=%d H=%d max_splits=%d need %zu bytes of split scratch; the allocation-free decode "
+                        "holds at most %zu (use mla_decode_nvfp4 with a workspace, or fewer splits)",
+                        B, H, max_splits, need, (size_t)MLA_DECODE_NOALLOC_SCRATCH_BYTES);
+    }
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (B > 0 && max_splits > 1) {
+        int rc = check_device();
+        if (rc) return rc;
+        rc = scratch_of_current_device(&ws);
+        if (rc) return rc;
+        ws_bytes = MLA_DECODE_NOALLOC_SCRATCH_BYTES;
+    }
+    return decode_entry(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                        page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                        ws, ws_bytes, out, lse, stream);
 }
 
 int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b,

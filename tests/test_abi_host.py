@@ -93,3 +93,15 @@ def test_other_entry_points_reject_invalid_arguments():
     # quantize_rows: K must be a multiple of 16
     assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 24, 1.0, 1 << 20, 1 << 20, None) == -1
     assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 32, 0.0, 1 << 20, 1 << 20, None) == -1
+
+
+def test_noalloc_decode_refuses_requests_beyond_its_scratch():
+    """The allocation-free decode checks its scratch limit on the host first."""
+    lib = L.lib()
+    args = _decode_args(B=600, H=128, splits=8)
+    del args[16:18]                           # no workspace arguments
+    assert lib.mla_decode_nvfp4_noalloc(*args) == -4
+    assert b"allocation-free" in lib.mla_last_error()
+    args = _decode_args(rec=400)
+    del args[16:18]
+    assert lib.mla_decode_nvfp4_noalloc(*args) == -2
