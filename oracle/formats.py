@@ -189,6 +189,30 @@ def nvfp4_qdq_ragged(x, g, axis: int = -1) -> np.ndarray:
     return float(F32(g)) * (e4m3_value(s) * e2m1_value(c))
 
 
+def fp8_quantize(x, g):
+    """Per-tensor FP8 quantization: one multiplier ``g`` (finite, > 0) for the
+    whole tensor ([MO-MLA], commit 1: the prefill operands may be NVFP4 in
+    1x16 blocks or per-tensor FP8).  The rule mirrors the NVFP4 element step:
+    inv = fp32(1 / g), code = e4m3(fp32(x * inv)) (RNE, satfinite, sign kept).
+    Returns the e4m3 codes."""
+    g = F32(g)
+    inv = (F32(1.0) / g).astype(F32)
+    return e4m3_encode((np.asarray(x, dtype=F32) * inv).astype(F32))
+
+
+def fp8_qdq(x, g) -> np.ndarray:
+    """Per-tensor FP8 fake quantization: float64 x_hat = g * value(code)."""
+    return float(F32(g)) * e4m3_value(fp8_quantize(x, g))
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of fp32 values, round to nearest even
+    (finite inputs)."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
 def bf16_to_f32(bits) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns (uint16) to fp32."""
     bits = np.asarray(bits, dtype=np.uint16).astype(np.uint32)

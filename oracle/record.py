@@ -28,7 +28,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (F32, bf16_to_f32, e2m1_value, e4m3_encode, e4m3_value,
-                      nvfp4_quantize)
+                      f32_to_bf16_bits, nvfp4_quantize)
 
 D_LATENT = 512
 D_ROPE = 64
@@ -94,6 +94,31 @@ def unpack_records(rec, outer_scale):
         bits = rec[..., r0:r0 + 2 * D_ROPE].copy().view("<u2")
         rope = bf16_to_f32(bits).astype(np.float64)
     return latent, rope
+
+
+def gather_bf16(rec, outer_scale):
+    """Cached-context gather: records back to the bf16 tensors a prefill over
+    the cached prefix consumes ([MO-MLA], commit 2: cached-context prefill
+    chunks are gathered from the quantized paged cache).  Latent element i:
+    one fp32 multiply of the outer scale by the exact value s * v, then
+    rounded to bf16 (nearest even).  RoPE: the stored bf16 value, or the e4m3
+    value (exact in bf16).  Returns uint16 bit patterns (kv_c [T,512],
+    k_pe [T,64])."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    fp8 = rope_is_fp8(rec.shape[-1])
+    packed = rec[..., :CODE_BYTES].astype(np.int64)
+    codes = np.empty(rec.shape[:-1] + (D_LATENT,), dtype=np.int64)
+    codes[..., 0::2] = packed & 0xF
+    codes[..., 1::2] = packed >> 4
+    scales = rec[..., CODE_BYTES:CODE_BYTES + SCALE_BYTES]
+    sv = (np.repeat(e4m3_value(scales), 16, axis=-1) * e2m1_value(codes)).astype(F32)   # exact
+    kv = f32_to_bf16_bits((F32(outer_scale) * sv).astype(F32))
+    r0 = CODE_BYTES + SCALE_BYTES
+    if fp8:
+        pe = f32_to_bf16_bits(e4m3_value(rec[..., r0:r0 + D_ROPE]).astype(F32))
+    else:
+        pe = rec[..., r0:r0 + 2 * D_ROPE].copy().view("<u2").astype(np.uint16)
+    return kv, pe
 
 
 def cache_write(cache, kv_c_bits, k_pe_bits, slot_mapping, outer_scale) -> None:
