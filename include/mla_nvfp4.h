@@ -66,11 +66,32 @@ typedef enum {
 /* Decode splits cover at least this many tokens (see mla_decode_num_splits). */
 #define MLA_DECODE_MIN_SPLIT_TOKENS 256
 
-/* qdq_flags bits of mla_prefill_nvfp4_out. */
+/* qdq_flags bits of mla_prefill_nvfp4_out and mla_prefill_attention.
+ * [MO-MLA], commit 1: every prefill matmul operand is fake-quantized once
+ * along its own contraction axis, as NVFP4 (1x16 blocks, e4m3 scale) or as
+ * per-tensor FP8; and new-token attention may carry token-exact N:M score
+ * sparsity.  MLA_QDQ_x switches operand x's quantization on (NVFP4 unless
+ * its MLA_QDQ_FP8_x bit is also set; an FP8 bit without its operand's bit is
+ * an error).  Per-tensor FP8 of x with multiplier g: code = e4m3(fp32(x *
+ * fp32(1/g))) (RNE, satfinite), x_hat = g * value(code); for P every element
+ * is quantized so with multiplier g_p (1/448 suits p <= 1). */
 #define MLA_QDQ_Q 1u
 #define MLA_QDQ_K 2u
 #define MLA_QDQ_P 4u
 #define MLA_QDQ_V 8u
+#define MLA_QDQ_FP8_Q 16u
+#define MLA_QDQ_FP8_K 32u
+#define MLA_QDQ_FP8_P 64u
+#define MLA_QDQ_FP8_V 128u
+#define MLA_QDQ_FP8_MASK 240u
+/* 2:4 score sparsity: in each group of 4 keys starting at a local key index
+ * divisible by 4, a query row keeps its 2 largest scores and masks the other
+ * two before the softmax; a key the row cannot see (causal mask, or past the
+ * end) ranks as -inf, and of equal scores the lower key index ranks first.
+ * The choice compares the fp32-accumulated scores (exact when Q and K are
+ * quantized; unquantized bf16 scores within rounding of each other may be
+ * chosen either way). */
+#define MLA_PREFILL_SPARSE_2_4 256u
 
 /* Thread-local text of the last error raised on this thread ("" if none). */
 const char* mla_last_error(void);
@@ -241,11 +262,13 @@ int mla_lse_merge(const float* partial_out, const float* partial_lse,
  * scale, the separate quantization pass removed).
  *
  * Sequence n covers rows [cu_seqlens[n], cu_seqlens[n+1]); queries and keys
- * of a sequence coincide; row i attends to keys j <= i.  Flags (MLA_QDQ_*):
- * Q and K quantized along the head dim (12 blocks of 16) with multipliers
- * g_q, g_k; V along local token position (blocks [16k,16k+16) from the
- * sequence start, the last one possibly short) per head and dim, with g_v;
- * P along keys with g_p, in blocks aligned to the local key index.  Keys are
+ * of a sequence coincide; row i attends to keys j <= i.  Flags (MLA_QDQ_*,
+ * MLA_PREFILL_SPARSE_2_4): Q and K quantized along the head dim (12 NVFP4
+ * blocks of 16, or per-tensor FP8) with multipliers g_q, g_k; V along local
+ * token position (NVFP4 blocks [16k,16k+16) from the sequence start, the
+ * last one possibly short, per head and dim; or per-tensor FP8) with g_v; P
+ * along keys with g_p, in NVFP4 blocks aligned to the local key index (or
+ * per-tensor FP8).  Keys are
  * visited in tiles of MLA_PREFILL_P_TILE = 64 from key 0; the running max is
  * refreshed per tile and P is quantized against it (the schedule is part of
  * the definition when MLA_QDQ_P is set).  O = acc / l, LSE = m + ln l, and
@@ -278,6 +301,76 @@ int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
                           void* workspace, size_t workspace_bytes,
                           uint8_t* out_fp4, uint8_t* out_scales, float* lse,
                           void* stream);
+
+/* Varlen prefill attention with fp32 output rows and LSE: the form a chunk of
+ * new tokens over cached context needs.  [MO-MLA], commit 1 (varlen prefill,
+ * operand quantization as above, natural-log LSE with which chunks of cached
+ * context merge) and commit 2 (cached-context chunks are gathered from the
+ * quantized paged cache and quantized again as prefill operands); [FUSED-OUT],
+ * gate conjuncts (the fused NVFP4 output is for batches without cached
+ * context: with context, the chunk outputs are merged first, then quantized).
+ *
+ * causal != 0: the keys of sequence n are its query rows [cu_seqlens_q[n],
+ * cu_seqlens_q[n+1]) of k and v, row i sees keys j <= i (as
+ * mla_prefill_nvfp4_out; cu_seqlens_k and T_k are ignored).  causal == 0:
+ * the keys of sequence n are rows [cu_seqlens_k[n], cu_seqlens_k[n+1]) of k
+ * and v (its cached context) and every query row sees all of them; a
+ * sequence without keys gives O = 0 and LSE = -inf.  V's NVFP4 token blocks
+ * start at each sequence's first key row; P's tile schedule is that of
+ * mla_prefill_nvfp4_out.  O (fp32) = acc / l with the dequant multipliers
+ * applied; LSE = m + ln l (natural log).
+ *
+ *  q            bf16 [T_q, H, 192]; k bf16 [T_k, H, 192]; v bf16 [T_k, H, 128]
+ *               (strides as in mla_prefill_nvfp4_out; finite values)
+ *  cu_seqlens_q int32 [N + 1], cu_seqlens_k int32 [N + 1] (context only),
+ *               non-decreasing from 0 to T_q and T_k
+ *  max_seqlen_q, max_seqlen_k  >= every sequence's query / key count
+ *  workspace    >= mla_prefill_workspace_bytes(T_k, H, qdq_flags) bytes
+ *               (T_q when causal)
+ *  out          fp32, element (t, h, d) at t*out_stride_t + h*out_stride_h + d
+ *               (strides multiples of 4, 16-byte aligned)
+ *  lse          fp32, (t, h) at t*lse_stride_t + h*lse_stride_h, or NULL
+ * A chunked prefill writes both parts into one [T_q, 2, H, 128] buffer
+ * (strides 256 H and 128, LSE strides 2 H and 1, the second part offset by
+ * 128 H and H) and merges them with mla_lse_merge (B = T_q, S = 2, D = 128).
+ * Preconditions (unchecked): cu arrays as stated. */
+int mla_prefill_attention(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h,
+                          const uint16_t* k, int64_t k_stride_t, int64_t k_stride_h,
+                          const uint16_t* v, int64_t v_stride_t, int64_t v_stride_h,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int N,
+                          int max_seqlen_q, int max_seqlen_k, int64_t T_q, int64_t T_k, int H,
+                          int causal, float softmax_scale, unsigned qdq_flags,
+                          float g_q, float g_k, float g_v, float g_p,
+                          void* workspace, size_t workspace_bytes,
+                          float* out, int64_t out_stride_t, int64_t out_stride_h,
+                          float* lse, int64_t lse_stride_t, int64_t lse_stride_h, void* stream);
+
+/* Gather cached context from the paged NVFP4 latent cache into bf16 rows.
+ * [MO-MLA], commit 2 (cached-context prefill chunks gather from the quantized
+ * paged cache); [B12X], walkthrough (records found through the block table,
+ * the per-layer outer scale restored on read).
+ *
+ * Output rows [cu_ctx[n], cu_ctx[n+1]) are positions ctx_start[n] + 0, 1, ...
+ * of sequence n (ctx_start NULL: from 0), position j being record
+ * page_table[n][j / page_size] * page_size + j % page_size.  Latent element:
+ * fp32(outer_scale * (s * v)) rounded to bf16 (nearest even), s * v being the
+ * exact e4m3-scale times e2m1 value; RoPE: the stored bf16 value, or the
+ * e4m3 value (exact in bf16).  A position past the page table or on a page
+ * id outside [0, num_pages) gives a zero row.
+ *
+ *  cache        uint8 [num_pages * page_size, record_bytes] (432 or 368)
+ *  page_table   int32 [N, max_pages_per_seq]
+ *  cu_ctx       int32 [N + 1], non-decreasing from 0 to T_ctx
+ *  ctx_start    int32 [N] or NULL
+ *  max_ctx_len  >= every cu_ctx[n+1] - cu_ctx[n]
+ *  kv_c_out     bf16 [T_ctx, 512], row stride (multiple of 8, 16-byte aligned)
+ *  k_pe_out     bf16 [T_ctx, 64], row stride (multiple of 8, 16-byte aligned) */
+int mla_nvfp4_cache_gather(const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                           const int32_t* page_table, int max_pages_per_seq,
+                           const int32_t* cu_ctx, const int32_t* ctx_start, int N, int max_ctx_len,
+                           int64_t T_ctx, float outer_scale,
+                           uint16_t* kv_c_out, int64_t kv_c_row_stride,
+                           uint16_t* k_pe_out, int64_t k_pe_row_stride, void* stream);
 
 /* NVFP4 quantization of fp32 rows with swizzled scales: the stand-alone
  * quantization pass that [FUSED-OUT] (PR description) folds into the prefill

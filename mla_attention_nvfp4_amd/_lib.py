@@ -38,10 +38,17 @@ SIGNATURES = {
     "mla_prefill_nvfp4_out": (c_int, [c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_int,
                                       c_int, c_i64, c_int, c_f32, c_u32, c_f32, c_f32, c_f32, c_f32, c_f32,
                                       c_p, c_sz, c_p, c_p, c_p, c_p]),
+    "mla_prefill_attention": (c_int, [c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_p, c_int,
+                                      c_int, c_int, c_i64, c_i64, c_int, c_int, c_f32, c_u32, c_f32, c_f32, c_f32,
+                                      c_f32, c_p, c_sz, c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p]),
+    "mla_nvfp4_cache_gather": (c_int, [c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_p, c_int, c_int, c_i64, c_f32,
+                                       c_p, c_i64, c_p, c_i64, c_p]),
     "mla_nvfp4_quantize_rows": (c_int, [c_p, c_i64, c_int, c_f32, c_p, c_p, c_p]),
 }
 
 MLA_QDQ_Q, MLA_QDQ_K, MLA_QDQ_P, MLA_QDQ_V = 1, 2, 4, 8
+MLA_QDQ_FP8_Q, MLA_QDQ_FP8_K, MLA_QDQ_FP8_P, MLA_QDQ_FP8_V = 16, 32, 64, 128
+MLA_PREFILL_SPARSE_2_4 = 256
 
 
 class MlaError(RuntimeError):
@@ -270,6 +277,73 @@ def prefill(q, k, v, cu_seqlens, max_seqlen, softmax_scale, flags, g_q, g_k, g_v
         float(out_global_scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
         codes.data_ptr(), scales.data_ptr(), _ptr(lse), _stream(q)))
     return codes, scales, lse
+
+
+def _check_qkv(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    if q.dim() != 3 or q.shape[2] != 192 or k.dim() != 3 or k.shape[1:] != q.shape[1:] or v.dim() != 3 \
+            or v.shape[0] != k.shape[0] or v.shape[1] != q.shape[1] or v.shape[2] != 128 \
+            or q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("q [Tq,H,192], k [Tk,H,192] and v [Tk,H,128] with unit inner stride")
+
+
+def prefill_attention(q, k, v, cu_seqlens_q, max_seqlen_q, softmax_scale, flags, g_q, g_k, g_v, g_p, causal=True,
+                      cu_seqlens_k=None, max_seqlen_k=0, out=None, lse=None, workspace=None):
+    """Varlen prefill attention with fp32 output.  causal: keys are the query
+    rows (k, v have q's rows); otherwise keys of sequence n are rows
+    [cu_seqlens_k[n], cu_seqlens_k[n+1]) of k and v (cached context).
+    ``out`` ([Tq,H,128] fp32, or a view with strides multiple of 4) and
+    ``lse`` ([Tq,H] fp32 view) may be passed in.  Returns (out, lse)."""
+    _check_qkv(q, k, v)
+    _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    Tq, H = q.shape[:2]
+    Tk = Tq if causal else k.shape[0]
+    if causal and k.shape[0] != Tq:
+        raise ValueError("causal attention: k and v have the query rows")
+    if not causal:
+        _need(cu_seqlens_k, torch.int32, "cu_seqlens_k")
+    dev = q.device
+    out = torch.empty((Tq, H, 128), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, torch.float32, "out")
+    _need(lse, torch.float32, "lse")
+    if out.shape != (Tq, H, 128) or out.stride(2) != 1 or lse.shape != (Tq, H):
+        raise ValueError("out must be [Tq,H,128] with unit inner stride and lse [Tq,H]")
+    need = prefill_workspace_bytes(Tk, H, flags)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().mla_prefill_attention(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1), v.data_ptr(), v.stride(0),
+        v.stride(1), cu_seqlens_q.data_ptr(), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, int(max_seqlen_q),
+        int(max_seqlen_k), Tq, Tk, H, 1 if causal else 0, float(softmax_scale), int(flags), float(g_q),
+        float(g_k), float(g_v), float(g_p), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        out.data_ptr(), out.stride(0), out.stride(1), lse.data_ptr(), lse.stride(0), lse.stride(1), _stream(q)))
+    return out, lse
+
+
+def cache_gather(cache, page_table, cu_ctx, max_ctx_len, outer_scale, ctx_start=None, kv_c=None, k_pe=None):
+    """Gather cached context rows from the paged NVFP4 cache into bf16
+    kv_c [T_ctx,512] and k_pe [T_ctx,64] (allocated unless given)."""
+    _need(cache, torch.uint8, "cache")
+    _need(page_table, torch.int32, "page_table")
+    _need(cu_ctx, torch.int32, "cu_ctx")
+    if cache.dim() != 3 or not cache.is_contiguous() or not page_table.is_contiguous() or page_table.dim() != 2:
+        raise ValueError("cache [num_pages, page_size, record_bytes] and page_table [N, max_pages], contiguous")
+    N = cu_ctx.numel() - 1
+    if page_table.shape[0] != N:
+        raise ValueError("page_table must have one row per sequence")
+    if ctx_start is not None:
+        _need(ctx_start, torch.int32, "ctx_start")
+    T = int(cu_ctx[-1].item()) if kv_c is None else kv_c.shape[0]
+    dev = cache.device
+    kv_c = torch.empty((T, 512), dtype=torch.bfloat16, device=dev) if kv_c is None else kv_c
+    k_pe = torch.empty((T, 64), dtype=torch.bfloat16, device=dev) if k_pe is None else k_pe
+    _check(lib().mla_nvfp4_cache_gather(
+        cache.data_ptr(), cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+        cu_ctx.data_ptr(), _ptr(ctx_start), N, int(max_ctx_len), T, float(outer_scale), kv_c.data_ptr(),
+        kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0), _stream(cache)))
+    return kv_c, k_pe
 
 
 def quantize_rows(x, global_scale):

@@ -356,6 +356,29 @@ size_t mla_prefill_workspace_bytes(int64_t T, int H, unsigned qdq_flags) {
     return mla::prefill_workspace_bytes(T, H, qdq_flags);
 }
 
+namespace {
+
+// Checks shared by the prefill entry points: flag bits, scales.
+int check_prefill_flags(unsigned flags, float softmax_scale, float g_q, float g_k, float g_v, float g_p) {
+    const unsigned known = 0xFu | MLA_QDQ_FP8_MASK | MLA_PREFILL_SPARSE_2_4;
+    if (flags & ~known) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown qdq_flags bits 0x%x", flags & ~known);
+    if ((flags & MLA_QDQ_FP8_MASK) >> 4 & ~flags & 0xFu)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "qdq_flags 0x%x: an FP8 format bit is set for an operand that is not "
+                    "quantized", flags);
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+    if (((flags & MLA_QDQ_Q) && !finite_pos(g_q)) || ((flags & MLA_QDQ_K) && !finite_pos(g_k)) ||
+        ((flags & MLA_QDQ_V) && !finite_pos(g_v)) || ((flags & MLA_QDQ_P) && !finite_pos(g_p)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "the scale of every enabled quantizer must be finite and > 0");
+    // a per-tensor FP8 multiplier must keep 1/g finite in fp32
+    if (((flags & MLA_QDQ_FP8_Q) && !std::isfinite(1.0f / g_q)) || ((flags & MLA_QDQ_FP8_K) && !std::isfinite(1.0f / g_k)) ||
+        ((flags & MLA_QDQ_FP8_V) && !std::isfinite(1.0f / g_v)) || ((flags & MLA_QDQ_FP8_P) && !std::isfinite(1.0f / g_p)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "a per-tensor FP8 multiplier is too small (1/g overflows)");
+    return MLA_OK;
+}
+
+}  // namespace
+
 int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, const uint16_t* k,
                           int64_t k_stride_t, int64_t k_stride_h, const uint16_t* v, int64_t v_stride_t,
                           int64_t v_stride_h, const int32_t* cu_seqlens, int N, int max_seqlen, int64_t T, int H,
@@ -364,12 +387,8 @@ int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
                           uint8_t* out_scales, float* lse, void* stream) {
     if (N < 0 || T < 0 || H < 1 || H > 1024 || max_seqlen < 0)
         return fail(MLA_ERR_INVALID_ARGUMENT, "need N >= 0, T >= 0, 1 <= H <= 1024, max_seqlen >= 0");
-    if (qdq_flags & ~15u) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown qdq_flags bits 0x%x", qdq_flags);
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
-    if (((qdq_flags & MLA_QDQ_Q) && !finite_pos(g_q)) || ((qdq_flags & MLA_QDQ_K) && !finite_pos(g_k)) ||
-        ((qdq_flags & MLA_QDQ_V) && !finite_pos(g_v)) || ((qdq_flags & MLA_QDQ_P) && !finite_pos(g_p)))
-        return fail(MLA_ERR_INVALID_ARGUMENT, "the scale of every enabled quantizer must be finite and > 0");
+    int rc0 = check_prefill_flags(qdq_flags, softmax_scale, g_q, g_k, g_v, g_p);
+    if (rc0) return rc0;
     if (!finite_pos(out_global_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "out_global_scale must be finite and > 0");
     if (T > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "T must fit in int32");
     if (T == 0 || N == 0) return ok();
@@ -389,20 +408,114 @@ int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
     a.k = k; a.k_st = k_stride_t; a.k_sh = k_stride_h;
     a.v = v; a.v_st = v_stride_t; a.v_sh = v_stride_h;
     a.cu_seqlens = cu_seqlens;
+    a.cu_k = nullptr;
     a.N = N;
     a.max_seqlen = max_seqlen;
+    a.max_seqlen_k = max_seqlen;
     a.T = T;
+    a.T_k = T;
     a.H = H;
+    a.causal = 1;
     a.softmax_scale = softmax_scale;
     a.flags = qdq_flags;
     a.g_q = g_q; a.g_k = g_k; a.g_v = g_v; a.g_p = g_p; a.g_out = out_global_scale;
     a.workspace = workspace;
     a.out_fp4 = out_fp4;
     a.out_scales = out_scales;
+    a.out_f32 = nullptr;
     a.lse = lse;
+    a.lse_st = H;
+    a.lse_sh = 1;
     hipError_t e = mla::launch_prefill(a, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(MLA_ERR_UNSUPPORTED, "prefill kernel not available");
     return hip_status(e, "prefill launch");
+}
+
+int mla_prefill_attention(const uint16_t* q, int64_t q_stride_t, int64_t q_stride_h, const uint16_t* k,
+                          int64_t k_stride_t, int64_t k_stride_h, const uint16_t* v, int64_t v_stride_t,
+                          int64_t v_stride_h, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int N,
+                          int max_seqlen_q, int max_seqlen_k, int64_t T_q, int64_t T_k, int H, int causal,
+                          float softmax_scale, unsigned qdq_flags, float g_q, float g_k, float g_v, float g_p,
+                          void* workspace, size_t workspace_bytes, float* out, int64_t out_stride_t,
+                          int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
+                          void* stream) {
+    if (N < 0 || T_q < 0 || H < 1 || H > 1024 || max_seqlen_q < 0)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need N >= 0, T_q >= 0, 1 <= H <= 1024, max_seqlen_q >= 0");
+    if (!causal && (T_k < 0 || max_seqlen_k < 0))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need T_k >= 0 and max_seqlen_k >= 0");
+    int rc = check_prefill_flags(qdq_flags, softmax_scale, g_q, g_k, g_v, g_p);
+    if (rc) return rc;
+    const int64_t Tk = causal ? T_q : T_k;
+    if (T_q > INT32_MAX || Tk > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "T_q and T_k must fit in int32");
+    if (T_q == 0 || N == 0) return ok();
+    if (!q || !cu_seqlens_q || !out || (!causal && !cu_seqlens_k) || (Tk > 0 && (!k || !v)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (q_stride_t % 8 || q_stride_h % 8 || k_stride_t % 8 || k_stride_h % 8 || v_stride_t % 8 || v_stride_h % 8 ||
+        !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "q/k/v strides must be multiples of 8 elements and 16-byte aligned");
+    if (out_stride_t % 4 || out_stride_h % 4 || !aligned(out, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "out strides must be multiples of 4 elements and out 16-byte aligned");
+    const size_t need = mla_prefill_workspace_bytes(Tk, H, qdq_flags);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need && !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    rc = check_device();
+    if (rc) return rc;
+    mla::PrefillArgs a{};
+    a.q = q; a.q_st = q_stride_t; a.q_sh = q_stride_h;
+    a.k = k; a.k_st = k_stride_t; a.k_sh = k_stride_h;
+    a.v = v; a.v_st = v_stride_t; a.v_sh = v_stride_h;
+    a.cu_seqlens = cu_seqlens_q;
+    a.cu_k = causal ? nullptr : cu_seqlens_k;
+    a.N = N;
+    a.max_seqlen = max_seqlen_q;
+    a.max_seqlen_k = causal ? max_seqlen_q : max_seqlen_k;
+    a.T = T_q;
+    a.T_k = Tk;
+    a.H = H;
+    a.causal = causal ? 1 : 0;
+    a.softmax_scale = softmax_scale;
+    a.flags = qdq_flags;
+    a.g_q = g_q; a.g_k = g_k; a.g_v = g_v; a.g_p = g_p; a.g_out = 1.0f;
+    a.workspace = workspace;
+    a.out_fp4 = nullptr;
+    a.out_scales = nullptr;
+    a.out_f32 = out;
+    a.o_st = out_stride_t;
+    a.o_sh = out_stride_h;
+    a.lse = lse;
+    a.lse_st = lse_stride_t;
+    a.lse_sh = lse_stride_h;
+    return hip_status(mla::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill attention launch");
+}
+
+int mla_nvfp4_cache_gather(const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                           const int32_t* page_table, int max_pages_per_seq, const int32_t* cu_ctx,
+                           const int32_t* ctx_start, int N, int max_ctx_len, int64_t T_ctx, float outer_scale,
+                           uint16_t* kv_c_out, int64_t kv_c_row_stride, uint16_t* k_pe_out,
+                           int64_t k_pe_row_stride, void* stream) {
+    int rc = check_record(record_bytes);
+    if (rc) return rc;
+    if (N < 0 || T_ctx < 0 || max_ctx_len < 0 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need N, T_ctx, max_ctx_len >= 0 and page_size, max_pages_per_seq, "
+                    "num_pages >= 1");
+    if ((int64_t)max_pages_per_seq * page_size > INT32_MAX)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq * page_size exceeds int32");
+    if (!finite_pos(outer_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "outer_scale must be finite and > 0");
+    if (N == 0 || T_ctx == 0 || max_ctx_len == 0) return ok();
+    if (!cache || !page_table || !cu_ctx || !kv_c_out || !k_pe_out)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (kv_c_row_stride % 8 || k_pe_row_stride % 8 || kv_c_row_stride < MLA_D_LATENT || k_pe_row_stride < MLA_D_ROPE ||
+        !aligned(kv_c_out, 16) || !aligned(k_pe_out, 16) || !aligned(cache, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "output rows must be 16-byte aligned with strides >= 512 / 64 "
+                    "(multiples of 8), and the cache 16-byte aligned");
+    rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_cache_gather(cache, num_pages, record_bytes == MLA_RECORD_BYTES_FP8_ROPE, page_size,
+                                               mla::page_recip_of(page_size), page_table, max_pages_per_seq, cu_ctx,
+                                               ctx_start, N, max_ctx_len, outer_scale, kv_c_out, kv_c_row_stride,
+                                               k_pe_out, k_pe_row_stride, static_cast<hipStream_t>(stream)),
+                      "cache gather launch");
 }
 
 int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale, uint8_t* codes,

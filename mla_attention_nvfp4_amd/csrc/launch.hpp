@@ -12,6 +12,14 @@ hipError_t launch_cache_write(const uint16_t* kv_c, int64_t kv_stride, const uin
                               uint8_t* cache, int64_t num_slots, bool rope_fp8, float g,
                               hipStream_t stream);
 
+// Cached-context gather: rows [cu_ctx[n], cu_ctx[n+1]) of the outputs are
+// positions ctx_start[n] (0 if null) onward of sequence n, dequantized.
+hipError_t launch_cache_gather(const uint8_t* cache, int64_t num_pages, bool rope_fp8, int page_size,
+                               uint32_t page_recip, const int32_t* page_table, int max_pages,
+                               const int32_t* cu_ctx, const int32_t* ctx_start, int N, int max_ctx_len,
+                               float g, uint16_t* kv_out, int64_t kv_stride, uint16_t* pe_out,
+                               int64_t pe_stride, hipStream_t stream);
+
 // Shared by dense and sparse decode.
 struct DecodeArgs {
     const uint16_t* q_nope;
@@ -55,21 +63,28 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_quantize_rows(const float* x, int64_t M, int K, float g, uint8_t* codes,
                                 uint8_t* scales, hipStream_t stream);
 
+// Prefill attention.  flags: 1 Q, 2 K, 4 P, 8 V quantized; 16/32/64/128 the
+// same operand as per-tensor FP8 instead of NVFP4; 256 2:4 score sparsity.
 struct PrefillArgs {
     const uint16_t* q; int64_t q_st, q_sh;
     const uint16_t* k; int64_t k_st, k_sh;
     const uint16_t* v; int64_t v_st, v_sh;
-    const int32_t* cu_seqlens;
-    int N, max_seqlen;
-    int64_t T;
+    const int32_t* cu_seqlens;   // query rows of each sequence
+    const int32_t* cu_k;         // key rows of each sequence (context attention; unused when causal)
+    int N, max_seqlen, max_seqlen_k;
+    int64_t T, T_k;              // query rows, key rows (T_k = T when causal)
     int H;
+    int causal;                  // keys are the query rows (row i sees keys j <= i)
     float softmax_scale;
     unsigned flags;
     float g_q, g_k, g_v, g_p, g_out;
     void* workspace;
-    uint8_t* out_fp4;
+    uint8_t* out_fp4;            // NVFP4 output (codes [T,H,64] + swizzled scales), or null:
     uint8_t* out_scales;
-    float* lse;
+    float* out_f32;              // fp32 rows, (t, h, d) at t*o_st + h*o_sh + d
+    int64_t o_st, o_sh;
+    float* lse;                  // (t, h) at t*lse_st + h*lse_sh, or null
+    int64_t lse_st, lse_sh;
 };
 
 size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags);

@@ -1,23 +1,31 @@
-// Varlen causal MLA prefill with NVFP4 fake quantization of Q/K/P/V and the
-// output written directly as NVFP4 (gfx950).
+// Varlen MLA prefill attention with NVFP4 or FP8 fake quantization of
+// Q/K/P/V, optional 2:4 score sparsity, and the output written directly as
+// NVFP4 or as fp32 rows with their LSE (gfx950).
 //
 // [MO-MLA], commit 1 and PR body: varlen prefill with asymmetric head dims
 // (qk 192, v 128); each matmul operand quantized once along its own
-// contraction axis in 1x16 NVFP4 blocks (Q, K along the head dim, V along
-// tokens, P along keys after the softmax row sum; the denominator stays
-// unquantized); natural-log LSE.  [FUSED-OUT], PR description: the output is
-// written as packed e2m1 codes plus e4m3 block scales in the 128x4-swizzled
-// layout with an fp32 global scale, replacing a separate quantization pass.
+// contraction axis, in 1x16 NVFP4 blocks or per-tensor FP8 (Q, K along the
+// head dim, V along tokens, P along keys after the softmax row sum; the
+// denominator stays unquantized); token-exact N:M score sparsity on the
+// new-token attention; natural-log LSE, with which chunks of cached context
+// merge.  [FUSED-OUT], PR description: the output is written as packed e2m1
+// codes plus e4m3 block scales in the 128x4-swizzled layout with an fp32
+// global scale, replacing a separate quantization pass (a path for batches
+// without cached context).
+//
+// Attention is causal (queries and keys are the same rows of a sequence) or
+// over a sequence's cached context (every query row sees every key row).
 //
 // Kernels:
 //   qk_qdq_kernel   K, one thread per 16-element block along d: the exact
-//                   bf16 value s*v of every element (the tensor-wide
-//                   multiplier g is applied later, in fp32).  Q takes the
-//                   same steps inside attn_kernel, on the rows it loads
-//                   (each Q row is read by one workgroup only);
-//   v_qdq_kernel    V, one thread per (16-token block of a sequence, head,
-//                   dim): blocks start at the sequence start, the last one
-//                   may be short;
+//                   bf16 value s*v (NVFP4) or e4m3 value (FP8) of every
+//                   element (the tensor-wide multiplier g is applied later,
+//                   in fp32).  Q takes the same steps inside attn_kernel, on
+//                   the rows it loads (each Q row is read by one workgroup);
+//   v_qdq_kernel    V (NVFP4), one thread per (16-token block of a sequence,
+//                   head, 8 dims): blocks start at the sequence start, the
+//                   last one may be short;
+//   v_fp8_kernel    V (FP8), 8 elements per thread;
 //   attn_kernel     one workgroup per (256 query rows, head, sequence):
 //                   8 wavefronts x 32 rows.  Keys are visited in tiles of 64
 //                   from key 0 (the P-quantization schedule), K/V tiles
@@ -30,7 +38,7 @@
 //                   iteration late, next to the softmax of wavefronts 0-3 on
 //                   the same SIMDs; V tiles are triple-buffered for that);
 //                   epilogue: O = acc * g_p g_v / l, NVFP4 codes and
-//                   swizzled scales, LSE = m + ln l;
+//                   swizzled scales (or fp32 rows), LSE = m + ln l;
 //   pad_scales_kernel  zero scale bytes of the padding rows of the last
 //                   128-row scale tile.
 #include "device_common.hpp"
@@ -57,11 +65,28 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- Q, K --
 
+// Per-tensor FP8 quantize-dequantize of 8 bf16 values (packed in w4) with
+// inv_g = fp32(1/g): code = e4m3(fp32(x * inv_g)) (RNE, satfinite, sign
+// kept), returned as the exact bf16 values of the codes (g not applied).
+__device__ __forceinline__ u32x4 fp8_qdq8_bf16(u32x4 w4, float inv_g) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t c2 = e4m3_encode2_hw(bf16_lo(w4[i]) * inv_g, bf16_hi(w4[i]) * inv_g);
+        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+        o[i] = pack_bf16_exact(d[0], d[1]);
+    }
+    return o;
+}
+
+template <bool kFp8>
 __global__ __launch_bounds__(256) void qk_qdq_kernel(const uint16_t* __restrict__ x, int64_t st, int64_t sh,
-                                                     int64_t T, int H, float g, uint16_t* __restrict__ out) {
+                                                     int64_t T, int H, float g, float inv_g,
+                                                     uint16_t* __restrict__ out) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // block of 16 along d
     const int64_t nblk = T * H * (kDqk / 16);
     if (idx >= nblk) return;
@@ -71,6 +96,12 @@ __global__ __launch_bounds__(256) void qk_qdq_kernel(const uint16_t* __restrict_
     const int64_t t = th / H;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + t * st + (int64_t)h * sh + 16 * blk);
     const u32x4 w0 = src[0], w1 = src[1];
+    if constexpr (kFp8) {
+        u32x4* dst = reinterpret_cast<u32x4*>(out + (t * H + h) * kDqk + 16 * blk);
+        dst[0] = fp8_qdq8_bf16(w0, inv_g);
+        dst[1] = fp8_qdq8_bf16(w1, inv_g);
+        return;
+    }
     float v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -156,26 +187,62 @@ __global__ __launch_bounds__(256) void v_qdq_kernel(const uint16_t* __restrict__
     }
 }
 
+// V as per-tensor FP8: rows [T, H, 128], 8 elements per thread; the exact
+// e4m3 values are written as fp16 (kF16Out) or bf16.
+template <bool kF16Out>
+__global__ __launch_bounds__(256) void v_fp8_kernel(const uint16_t* __restrict__ v, int64_t st, int64_t sh,
+                                                    int64_t T, int H, float inv_g, uint16_t* __restrict__ out) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (token, head, 8 dims)
+    if (idx >= T * H * (kDv / 8)) return;
+    const int d0 = 8 * (int)(idx % (kDv / 8));
+    const int64_t th = idx / (kDv / 8);
+    const int h = (int)(th % H);
+    const int64_t t = th / H;
+    const u32x4 w4 = *reinterpret_cast<const u32x4*>(v + t * st + (int64_t)h * sh + d0);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t c2 = e4m3_encode2_hw(bf16_lo(w4[i]) * inv_g, bf16_hi(w4[i]) * inv_g);
+        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+        if constexpr (kF16Out) {
+            const f16x2v hv = {(_Float16)d[0], (_Float16)d[1]};
+            o[i] = __builtin_bit_cast(uint32_t, hv);
+        } else {
+            o[i] = pack_bf16_exact(d[0], d[1]);
+        }
+    }
+    *reinterpret_cast<u32x4*>(out + (t * H + h) * kDv + d0) = o;
+}
+
 // ----------------------------------------------------------- attention --
 
 struct AttnParams {
     const uint16_t* q; int64_t q_st, q_sh;   // raw Q
     int q_qdq;                // Q quantize-dequantized on load (multiplier q_g)
-    float q_g;
+    int q_fp8;                // ... as per-tensor FP8 (q_inv = fp32(1/q_g)) instead of NVFP4
+    float q_g, q_inv;
     const uint16_t* k; int64_t k_st, k_sh;
     const uint16_t* v; int64_t v_st, v_sh;
-    const int32_t* cu;
+    const int32_t* cu;        // query rows of sequence n: [cu[n], cu[n+1])
+    const int32_t* ck;        // key rows of sequence n (context attention): [ck[n], ck[n+1])
+    int causal;               // keys are the query rows, row i sees keys j <= i
+    int sparse24;             // 2:4 score sparsity
+    int score_pos;            // softmax_scale > 0 (else every score ties for the 2:4 choice)
     int H;
     float score_scale_log2;   // softmax_scale * g_q' * g_k' * log2(e)
     double out_scale;         // g_p' * g_v' (exact in fp64)
     float g_p;                // P multiplier (P quantized only)
     float u_p;                // fp32(6 g_p)
     float inv_u_p;            // fp32(1 / u_p)
+    float inv_g_p;            // fp32(1 / g_p) (P as FP8)
     float g_out;              // output global scale
     int64_t T;
-    uint8_t* out_fp4;
+    uint8_t* out_fp4;         // NVFP4 output (null: fp32 rows to out_f32)
     uint8_t* out_scales;
-    float* lse;
+    float* out_f32;           // fp32 output rows: element (t, h, d) at t*o_st + h*o_sh + d
+    int64_t o_st, o_sh;
+    float* lse;               // (t, h) at t*lse_st + h*lse_sh
+    int64_t lse_st, lse_sh;
 };
 
 struct AttnSmem {
@@ -217,15 +284,22 @@ struct BoolTag {
 // (slot j <-> key 16kb + 8(j/4) + 4 g2 + j%4; the V^T operand uses the same
 // slots).
 //
-// kF16: P and V are both quantized, so P^ = s*v and V^ = s*v are exact in
-// fp16 and the PV products run in fp16, P^ coming straight from the FP4
-// conversion; otherwise they run in bf16 (quantized P exact, unquantized P
-// split into three bf16 parts).
-template <bool kQuantP, bool kF16>
+// kPMode: 0 P unquantized, 1 NVFP4 blocks along keys, 2 per-tensor FP8.
+// kF16: P and V are both quantized, so P^ (s*v or an e4m3 value) and V^ are
+// exact in fp16 and the PV products run in fp16, P^ coming straight from the
+// FP4 or FP8 conversion; otherwise they run in bf16 (quantized P exact,
+// unquantized P split into three bf16 parts).
+//
+// 2:4 sparsity: in a score tile, a lane's elements 4c .. 4c+3 are 4
+// consecutive keys starting at a multiple of 4, so each group's choice is
+// made within one lane, on the raw fp32 accumulators (the scale factors are
+// common to the row and positive; softmax_scale = 0 makes every score tie).
+template <int kPMode, bool kF16>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnParams p) {
+    constexpr bool kQuantP = kPMode != 0;
     __shared__ AttnSmem sm;
-    if (kQuantP && threadIdx.x < 256) {
+    if (kPMode == 1 && threadIdx.x < 256) {
         const float d = e4m3_decode(threadIdx.x) * p.g_p;
         sm.pinv[threadIdx.x] = (d == 0.0f) ? 0.0f : 1.0f / d;
     }
@@ -236,9 +310,11 @@ void attn_kernel(AttnParams p) {
     decode_work_item((int)gridDim.x, (int)(gridDim.y * gridDim.z), qx, u);
     const int h = u % (int)gridDim.y, n = u / (int)gridDim.y;
     const int a = p.cu[n], e = p.cu[n + 1];
-    const int L = e - a;
+    const int L = e - a;                                  // query rows
+    const int ka = p.causal ? a : p.ck[n];                // first key row
+    const int Lk = p.causal ? L : p.ck[n + 1] - ka;       // key rows
     const int nqt = (L + kBM - 1) / kBM;
-    const int qt = nqt - 1 - qx;   // longest (latest) tiles first
+    const int qt = nqt - 1 - qx;   // (causal) longest, latest tiles first
     if (qt < 0) return;
     const int r0 = qt * kBM;                     // local row of the tile
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -246,6 +322,7 @@ void attn_kernel(AttnParams p) {
     const int wr0 = r0 + kRowsPerWave * w;       // first local row of this wavefront
     const bool wave_rows = wr0 < L;
     const int row = wr0 + l32;                   // this lane's query row
+    const int lim = p.causal ? row : Lk - 1;     // last key this row sees
 
     // Q row (B operand of S^T = K Q^T): k-step kk covers dims 16kk + 8 g2 .. +7
     bf16x8 qf[12];
@@ -257,7 +334,10 @@ void attn_kernel(AttnParams p) {
     }
     // Q quantize-dequantize, the same steps as qk_qdq_kernel: block kk of
     // the row is this lane's 8 values and those of lane ^ 32
-    if (p.q_qdq) {
+    if (p.q_qdq && p.q_fp8) {
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) qf[kk] = as_bf16x8(fp8_qdq8_bf16(__builtin_bit_cast(u32x4, qf[kk]), p.q_inv));
+    } else if (p.q_qdq) {
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) {
             const u32x4 w4 = __builtin_bit_cast(u32x4, qf[kk]);
@@ -283,9 +363,10 @@ void attn_kernel(AttnParams p) {
         }
     }
 
-    // last key tile this workgroup needs; a wavefront needs tiles up to its last row
+    // last key tile this workgroup needs; (causal) a wavefront needs tiles up
+    // to its last row
     const int rows_end = min(r0 + kBM, L);
-    const int nkt = (rows_end + kBN - 1) / kBN;
+    const int nkt = p.causal ? (rows_end + kBN - 1) / kBN : (Lk + kBN - 1) / kBN;
     const int wave_last_row = min(wr0 + kRowsPerWave, L) - 1;
 
     // K/V tile staging: K 64 rows x 24 chunks (3 per thread), V 64 x 16 (2 per thread)
@@ -294,14 +375,14 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             const int c = tid + 512 * i;
-            const int j = min(kt * kBN + c / 24, L - 1);
-            sk[i] = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(a + j) * p.k_st + (int64_t)h * p.k_sh + 8 * (c % 24));
+            const int j = min(kt * kBN + c / 24, Lk - 1);
+            sk[i] = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(ka + j) * p.k_st + (int64_t)h * p.k_sh + 8 * (c % 24));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 512 * i;
-            const int j = min(kt * kBN + (c >> 4), L - 1);
-            sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(a + j) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15));
+            const int j = min(kt * kBN + (c >> 4), Lk - 1);
+            sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(ka + j) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15));
         }
     };
     auto store_tile = [&](int buf, int vbuf) {
@@ -387,20 +468,53 @@ void attn_kernel(AttnParams p) {
         // since fp32(c x) is monotone in x for c >= 0, and each exponent is
         // one fused c * s - m)
         float mx = -INFINITY;
+        if constexpr (kMask) {
+            // keys past this row's last key are masked; with 2:4 sparsity,
+            // of each group of 4 the keys outranked by two others too
+            // bit 16 mt2 + v of vis: element v of score tile mt2 is seen
+            const int rel = lim - (kt * kBN + 4 * g2);   // last key offset this lane's row sees
+            uint32_t vis = 0u;
 #pragma unroll
-        for (int mt2 = 0; mt2 < 2; ++mt2)
+            for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                if constexpr (kMask) {
-                    float z = c_log2 * s[mt2][v];
-                    const int key = kt * kBN + 32 * mt2 + 8 * (v >> 2) + 4 * g2 + (v & 3);
-                    z = key <= row ? z : -INFINITY;
+                for (int v = 0; v < 16; ++v)
+                    vis |= (32 * mt2 + 8 * (v >> 2) + (v & 3) <= rel ? 1u : 0u) << (16 * mt2 + v);
+            if (p.sparse24) {   // (uniform)
+#pragma unroll
+                for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int b0 = 16 * mt2 + 4 * c;
+                        float x[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x[i] = ((vis >> (b0 + i)) & 1u) ? (p.score_pos ? s[mt2][4 * c + i] : 0.0f) : -INFINITY;
+                        uint32_t drop = 0u;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            int rank = 0;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                if (j != i) rank += (x[j] > x[i] || (x[j] == x[i] && j < i)) ? 1 : 0;
+                            drop |= (rank >= 2 ? 1u : 0u) << (b0 + i);
+                        }
+                        vis &= ~drop;
+                    }
+            }
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float z = ((vis >> (16 * mt2 + v)) & 1u) ? c_log2 * s[mt2][v] : -INFINITY;
                     s[mt2][v] = z;
                     mx = fmaxf(mx, z);
-                } else {
-                    mx = fmaxf(mx, s[mt2][v]);
                 }
-            }
+        } else {
+#pragma unroll
+            for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mt2][v]);
+        }
         mx = xor32_max(mx);
         if constexpr (!kMask) mx = c_log2 * mx;
         const float m_new = fmaxf(m_run, mx);
@@ -425,7 +539,31 @@ void attn_kernel(AttnParams p) {
         }
         // ---- P operands per 16-key block kb
         bf16x8 ph[4], pm[4], pl[4];
-        if constexpr (kQuantP) {
+        if constexpr (kPMode == 2) {
+            // per-tensor FP8: code = e4m3(fp32(p * fp32(1/g_p))) (p >= 0),
+            // its exact value in the fp16 or bf16 operand
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x16& t = s[kb >> 1];
+                const int o8 = 8 * (kb & 1);
+                float d[8];
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const uint32_t c2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                        fminf(t[o8 + i] * p.inv_g_p, 448.0f), fminf(t[o8 + i + 1] * p.inv_g_p, 448.0f), 0, false);
+                    const f32x2 dv = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+                    d[i] = dv[0];
+                    d[i + 1] = dv[1];
+                }
+                if constexpr (kF16) {
+                    hold[kb] = f16x8{(_Float16)d[0], (_Float16)d[1], (_Float16)d[2], (_Float16)d[3],
+                                     (_Float16)d[4], (_Float16)d[5], (_Float16)d[6], (_Float16)d[7]};
+                } else {
+                    ph[kb] = as_bf16x8(u32x4{pack_bf16_exact(d[0], d[1]), pack_bf16_exact(d[2], d[3]),
+                                             pack_bf16_exact(d[4], d[5]), pack_bf16_exact(d[6], d[7])});
+                }
+            }
+        } else if constexpr (kQuantP) {
             // block amax, then the four blocks' scales side by side (the rare
             // exact divisions in one uniform branch)
             float am[4], tq[4];
@@ -538,8 +676,10 @@ void attn_kernel(AttnParams p) {
         }
     };
 
-    load_tile(0);
-    store_tile(0, 0);
+    if (nkt > 0) {
+        load_tile(0);
+        store_tile(0, 0);
+    }
     if (nkt > 1) load_tile(1);
     __syncthreads();
     // With P and V quantized, wavefronts 4-7 (which share SIMDs with 0-3)
@@ -560,10 +700,12 @@ void attn_kernel(AttnParams p) {
                 held = -1;
             }
         }
-        // a wavefront skips tiles that start after its last row; tiles
-        // entirely at or below its first row need no causal mask
-        if (wave_rows && kt * kBN <= wave_last_row) {
-            if (kt * kBN + kBN - 1 <= wr0) compute(kt, kt & 1, vbuf, BoolTag<false>{}, defer);
+        // (causal) a wavefront skips tiles that start after its last row;
+        // tiles whose keys all lie within every row's reach need no mask
+        // (unless the 2:4 choice masks keys)
+        if (wave_rows && (!p.causal || kt * kBN <= wave_last_row)) {
+            const bool full = p.causal ? kt * kBN + kBN - 1 <= wr0 : kt * kBN + kBN <= Lk;
+            if (full && !p.sparse24) compute(kt, kt & 1, vbuf, BoolTag<false>{}, defer);
             else compute(kt, kt & 1, vbuf, BoolTag<true>{}, defer);
             if constexpr (kQuantP && kF16) {
                 if (defer) held = vbuf;
@@ -587,6 +729,28 @@ void attn_kernel(AttnParams p) {
     const bool ok = row < L;
     const double inv_l = l_run > 0.0f ? p.out_scale / (double)l_run : 0.0;
     const int64_t t = a + row;
+    const float lse_v = l_run > 0.0f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    if (!p.out_fp4) {
+        // fp32 rows: block b's elements 0..3 are dims 16b + 4 g2 + 0..3, 4..7
+        // are dims 16b + 8 + 4 g2 + 0..3 (a row without keys is 0, lse -inf)
+        if (!ok) return;
+        float* dst = p.out_f32 + t * p.o_st + (int64_t)h * p.o_sh + 4 * g2;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const f32x16& ob = o[b >> 1];
+            const int o8 = 8 * (b & 1);
+            f32x4 lo, hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo[i] = (float)((double)ob[o8 + i] * inv_l);
+                hi[i] = (float)((double)ob[o8 + 4 + i] * inv_l);
+            }
+            *reinterpret_cast<f32x4*>(dst + 16 * b) = lo;
+            *reinterpret_cast<f32x4*>(dst + 16 * b + 8) = hi;
+        }
+        if (g2 == 0 && p.lse) p.lse[t * p.lse_st + (int64_t)h * p.lse_sh] = lse_v;
+        return;
+    }
     uint8_t* codes_row = p.out_fp4 + (t * p.H + h) * (kDv / 2);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -612,8 +776,7 @@ void attn_kernel(AttnParams p) {
             }
         }
     }
-    if (ok && g2 == 0 && p.lse)
-        p.lse[t * p.H + h] = l_run > 0.0f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    if (ok && g2 == 0 && p.lse) p.lse[t * p.lse_st + (int64_t)h * p.lse_sh] = lse_v;
 }
 
 // Zero the scale bytes of rows T .. ceil(T/128)*128 - 1 (all columns).
@@ -641,64 +804,105 @@ size_t prefill_workspace_bytes(int64_t T, int H, unsigned flags) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int H = a.H;
     const int64_t T = a.T;
+    const bool causal = a.causal != 0;
+    const int64_t Tk = causal ? T : a.T_k;
+    const int32_t* cuk = causal ? a.cu_seqlens : a.cu_k;
+    const int max_k = causal ? a.max_seqlen : a.max_seqlen_k;
+    const unsigned f = a.flags;
+    const bool qP = f & 4u, qV = f & 8u;
     uint16_t* ws = static_cast<uint16_t*>(a.workspace);
     AttnParams p{};
     p.q = a.q; p.q_st = a.q_st; p.q_sh = a.q_sh;
     p.k = a.k; p.k_st = a.k_st; p.k_sh = a.k_sh;
     p.v = a.v; p.v_st = a.v_st; p.v_sh = a.v_sh;
     float gq = 1.0f, gk = 1.0f, gv = 1.0f, gp = 1.0f;
-    const int64_t nqk_blocks = T * H * (kDqk / 16);
-    if (a.flags & 1u) {   // (in attn_kernel)
+    if (f & 1u) {   // (in attn_kernel)
         p.q_qdq = 1;
+        p.q_fp8 = (f & 16u) ? 1 : 0;
         p.q_g = a.g_q;
+        p.q_inv = 1.0f / a.g_q;
         gq = a.g_q;
     }
-    if (a.flags & 2u) {
-        hipLaunchKernelGGL(qk_qdq_kernel, dim3((unsigned)((nqk_blocks + 255) / 256)), dim3(256), 0, stream, a.k,
-                           a.k_st, a.k_sh, T, H, a.g_k, ws);
-        p.k = ws; p.k_st = (int64_t)H * kDqk; p.k_sh = kDqk;
-        gk = a.g_k;
-        ws += (size_t)T * H * kDqk;
-    }
-    if (a.flags & 8u) {
-        const dim3 grid((unsigned)((a.max_seqlen + 15) / 16), (unsigned)a.N, (unsigned)((H * (kDv / 8) + 255) / 256));
-        if (a.flags & 4u)
-            hipLaunchKernelGGL(v_qdq_kernel<true>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens, H,
-                               a.g_v, ws);
+    if ((f & 2u) && Tk > 0) {
+        const int64_t nqk_blocks = Tk * H * (kDqk / 16);
+        const dim3 grid((unsigned)((nqk_blocks + 255) / 256));
+        if (f & 32u)
+            hipLaunchKernelGGL(qk_qdq_kernel<true>, grid, dim3(256), 0, stream, a.k, a.k_st, a.k_sh, Tk, H, a.g_k,
+                               1.0f / a.g_k, ws);
         else
-            hipLaunchKernelGGL(v_qdq_kernel<false>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, a.cu_seqlens,
-                               H, a.g_v, ws);
-        p.v = ws; p.v_st = (int64_t)H * kDv; p.v_sh = kDv;
-        gv = a.g_v;
-        ws += (size_t)T * H * kDv;
+            hipLaunchKernelGGL(qk_qdq_kernel<false>, grid, dim3(256), 0, stream, a.k, a.k_st, a.k_sh, Tk, H, a.g_k,
+                               1.0f / a.g_k, ws);
+        p.k = ws; p.k_st = (int64_t)H * kDqk; p.k_sh = kDqk;
+        ws += (size_t)Tk * H * kDqk;
     }
-    if (a.flags & 4u) gp = a.g_p;
+    if (f & 2u) gk = a.g_k;
+    if (qV && Tk > 0) {
+        if (f & 128u) {
+            const int64_t n8 = Tk * H * (kDv / 8);
+            const dim3 grid((unsigned)((n8 + 255) / 256));
+            if (qP)
+                hipLaunchKernelGGL(v_fp8_kernel<true>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, Tk, H,
+                                   1.0f / a.g_v, ws);
+            else
+                hipLaunchKernelGGL(v_fp8_kernel<false>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, Tk, H,
+                                   1.0f / a.g_v, ws);
+        } else {
+            const dim3 grid((unsigned)((max_k + 15) / 16), (unsigned)a.N, (unsigned)((H * (kDv / 8) + 255) / 256));
+            if (qP)
+                hipLaunchKernelGGL(v_qdq_kernel<true>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, cuk, H,
+                                   a.g_v, ws);
+            else
+                hipLaunchKernelGGL(v_qdq_kernel<false>, grid, dim3(256), 0, stream, a.v, a.v_st, a.v_sh, cuk, H,
+                                   a.g_v, ws);
+        }
+        p.v = ws; p.v_st = (int64_t)H * kDv; p.v_sh = kDv;
+        ws += (size_t)Tk * H * kDv;
+    }
+    if (qV) gv = a.g_v;
+    if (qP) gp = a.g_p;
     p.cu = a.cu_seqlens;
+    p.ck = cuk;
+    p.causal = causal ? 1 : 0;
+    p.sparse24 = (f & 256u) ? 1 : 0;
+    p.score_pos = a.softmax_scale > 0.0f ? 1 : 0;
     p.H = H;
     p.score_scale_log2 = a.softmax_scale * gq * gk * kLog2e;
     p.out_scale = (double)gp * (double)gv;
     p.g_p = a.g_p;
     p.u_p = 6.0f * a.g_p;
     p.inv_u_p = 1.0f / p.u_p;
+    p.inv_g_p = 1.0f / a.g_p;
     p.g_out = a.g_out;
     p.T = T;
     p.out_fp4 = a.out_fp4;
     p.out_scales = a.out_scales;
+    p.out_f32 = a.out_f32;
+    p.o_st = a.o_st;
+    p.o_sh = a.o_sh;
     p.lse = a.lse;
+    p.lse_st = a.lse_st;
+    p.lse_sh = a.lse_sh;
     if (a.max_seqlen > 0) {
         const dim3 grid((unsigned)((a.max_seqlen + kBM - 1) / kBM), (unsigned)H, (unsigned)a.N);
-        if ((a.flags & 4u) && (a.flags & 8u))
-            hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kWaves * 64), 0, stream, p);
-        else if (a.flags & 4u)
-            hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kWaves * 64), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kWaves * 64), 0, stream, p);
+        const dim3 block(kWaves * 64);
+        const bool fp8p = f & 64u;
+        if (qP && qV) {
+            if (fp8p) hipLaunchKernelGGL((attn_kernel<2, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((attn_kernel<1, true>), grid, block, 0, stream, p);
+        } else if (qP) {
+            if (fp8p) hipLaunchKernelGGL((attn_kernel<2, false>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((attn_kernel<1, false>), grid, block, 0, stream, p);
+        } else {
+            hipLaunchKernelGGL((attn_kernel<0, false>), grid, block, 0, stream, p);
+        }
     }
-    const int64_t cpad = (int64_t)H * 8;
-    const int64_t npad = ((T + 127) / 128 * 128 - T) * cpad;
-    if (npad > 0)
-        hipLaunchKernelGGL(pad_scales_kernel, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, stream,
-                           a.out_scales, T, cpad);
+    if (a.out_fp4) {
+        const int64_t cpad = (int64_t)H * 8;
+        const int64_t npad = ((T + 127) / 128 * 128 - T) * cpad;
+        if (npad > 0)
+            hipLaunchKernelGGL(pad_scales_kernel, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, stream,
+                               a.out_scales, T, cpad);
+    }
     return hipGetLastError();
 }
 

@@ -210,9 +210,25 @@ class PrefillInputs:
         return int(self.cu_seqlens[-1])
 
 
-def _amax_scale(x: torch.Tensor) -> float:
-    # the caller's tensor-wide multiplier: fp32(max|x| / (6 * 448))
-    return float(np.float32(float(x.abs().max().float()) / 2688.0))
+FP8_BIT = {"q": 16, "k": 32, "p": 64, "v": 128}
+
+
+def _amax_scale(x: torch.Tensor, fp8: bool = False) -> float:
+    # the caller's tensor-wide multiplier: fp32(max|x| / (6 * 448)) for NVFP4
+    # (block scales up to 448 times elements up to 6), fp32(max|x| / 448) for
+    # per-tensor FP8
+    return float(np.float32(float(x.abs().max().float()) / (448.0 if fp8 else 2688.0)))
+
+
+def _p_scale(flags: int) -> float:
+    # probabilities are at most 1: fp32(1 / 448) for FP8, fp32(1 / (6 * 448)) for NVFP4
+    return float(np.float32(1.0 / (448.0 if flags & FP8_BIT["p"] else 2688.0)))
+
+
+def _cu(lens) -> torch.Tensor:
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int32), 0)
+    return cu
 
 
 def prefill_inputs(seed: int, lens, H: int, flags: int = 15, name: str | None = None) -> PrefillInputs:
@@ -222,12 +238,57 @@ def prefill_inputs(seed: int, lens, H: int, flags: int = 15, name: str | None = 
     q = _randn_bf16(g, (T, H, 192), chunk_rows=4096)
     k = _randn_bf16(g, (T, H, 192), chunk_rows=4096)
     v = _randn_bf16(g, (T, H, 128), chunk_rows=4096)
-    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
-    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int32), 0)
-    gq, gk, gv = (_amax_scale(t) if T else 1.0 for t in (q, k, v))
-    return PrefillInputs(name=name or f"prefill{seed}", H=H, q=q, k=k, v=v, cu_seqlens=cu,
+    gq, gk, gv = (_amax_scale(t, bool(flags & FP8_BIT[n])) if T else 1.0 for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    return PrefillInputs(name=name or f"prefill{seed}", H=H, q=q, k=k, v=v, cu_seqlens=_cu(lens),
                          max_seqlen=max(lens) if lens else 0, softmax_scale=1.0 / math.sqrt(192),
-                         flags=flags, g_q=gq, g_k=gk, g_v=gv, g_p=float(np.float32(1.0 / 2688.0)), g_out=gv)
+                         flags=flags, g_q=gq, g_k=gk, g_v=gv, g_p=_p_scale(flags), g_out=gv)
+
+
+def grid_prefill_inputs(seed: int, lens, H: int, flags: int, name: str | None = None) -> PrefillInputs:
+    """As prefill_inputs, but Q and K drawn from the grid {-1, -0.75, ..., 1}:
+    every score is then a multiple of 1/16 below 192 in magnitude (exact in
+    fp32 whatever the summation order), and equal scores are common."""
+    inp = prefill_inputs(seed, lens, H, flags, name)
+    g = torch.Generator().manual_seed(seed + 7919)
+    T = inp.T
+    inp.q = (torch.randint(-4, 5, (T, H, 192), generator=g).float() / 4).to(torch.bfloat16)
+    inp.k = (torch.randint(-4, 5, (T, H, 192), generator=g).float() / 4).to(torch.bfloat16)
+    if T:
+        inp.g_q = _amax_scale(inp.q, bool(flags & FP8_BIT["q"]))
+        inp.g_k = _amax_scale(inp.k, bool(flags & FP8_BIT["k"]))
+    return inp
+
+
+@dataclasses.dataclass
+class ContextInputs:
+    """A chunk of new tokens per sequence plus that sequence's cached context
+    as prefill operands (the model's projection of the gathered latent):
+    q, k, v new-token rows [T, H, 192/192/128] with cu_q; ctx_k, ctx_v
+    context rows [Tc, H, 192/128] with cu_ctx."""
+    new: PrefillInputs
+    ctx_k: torch.Tensor
+    ctx_v: torch.Tensor
+    cu_ctx: torch.Tensor
+
+    @property
+    def max_ctx(self) -> int:
+        c = self.cu_ctx.tolist()
+        return max([b - a for a, b in zip(c[:-1], c[1:])] + [0])
+
+
+def context_inputs(seed: int, new_lens, ctx_lens, H: int, flags: int) -> ContextInputs:
+    """Seeded new-token and context operands, N(0,1) rounded to bf16; K and V
+    multipliers cover both (their amax over new and context rows)."""
+    new = prefill_inputs(seed, new_lens, H, flags)
+    g = torch.Generator().manual_seed(seed + 104729)
+    Tc = sum(int(x) for x in ctx_lens)
+    ck = _randn_bf16(g, (Tc, H, 192), chunk_rows=4096)
+    cv = _randn_bf16(g, (Tc, H, 128), chunk_rows=4096)
+    if Tc and new.T:
+        new.g_k = _amax_scale(torch.cat([new.k.reshape(-1), ck.reshape(-1)]), bool(flags & FP8_BIT["k"]))
+        new.g_v = _amax_scale(torch.cat([new.v.reshape(-1), cv.reshape(-1)]), bool(flags & FP8_BIT["v"]))
+        new.g_out = new.g_v
+    return ContextInputs(new=new, ctx_k=ck, ctx_v=cv, cu_ctx=_cu(ctx_lens))
 
 
 def prefill_workload(n: int = 4) -> PrefillInputs:

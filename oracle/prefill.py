@@ -131,7 +131,7 @@ def keep_2_4(score, valid):
 
 
 def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p, p_quantizer=None, *,
-                causal=True, sparse_2_4=False, p_fp8=False, multipliers=(1.0, 1.0)):
+                causal=True, sparse_2_4=False, p_fp8=False, multipliers=(1.0, 1.0), keep_fn=None):
     """Steps 2-4 for one sequence and one head.
 
     qh [Lq,192], kh [Lk,192], vh [Lk,128] (this sequence, float64); ``rows``
@@ -144,7 +144,8 @@ def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p, p_quantizer=No
     ``p_quantizer(p32, t0)``, if given, replaces step 3's P QDQ for the tile
     starting at key t0 (p32: the tile's fp32 probabilities [R, 64]); it lets a
     test examine the alternatives of P rounding decisions that lie on a
-    rounding boundary.
+    rounding boundary.  ``keep_fn(score, valid)``, likewise, replaces the 2:4
+    choice (``keep_2_4``), for the alternatives of near-equal scores.
     """
     rows = np.asarray(rows, dtype=np.int64)
     R = rows.size
@@ -161,7 +162,7 @@ def attend_rows(qh, kh, vh, rows, softmax_scale, quantize_p, g_p, p_quantizer=No
             exact[:, :nk] = (qh[rows] / multipliers[0]) @ (kh[:nk] / multipliers[1]).T
         keys4 = np.arange(n4)
         valid4 = (keys4[None, :] <= rows[:, None]) if causal else np.broadcast_to(keys4 < nk, (R, n4))
-        kept = keep_2_4(exact, valid4)[:, :nk]
+        kept = (keep_fn or keep_2_4)(exact, valid4)[:, :nk]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, D_V))

@@ -79,12 +79,23 @@ def _valid(x, gs, gv, g):
     return ok.reshape(x.shape)
 
 
-def _block_options(p16, g):
-    """All NVFP4 QDQ results (float64 [16]) of one P block whose fp32 values
-    the GPU knows only to within DELTA relative: the oracle's own result first,
-    then those from the other side of any e4m3 or e2m1 rounding boundary
-    within reach."""
+def _block_options(p16, g, fp8=False):
+    """All QDQ results (float64 [16]) of one P block whose fp32 values the GPU
+    knows only to within DELTA relative: the oracle's own result first, then
+    those from the other side of any e4m3 or e2m1 rounding boundary within
+    reach (NVFP4), or of any element's e4m3 boundary (per-tensor FP8)."""
     g32 = np.float32(g)
+    if fp8:
+        inv = np.float32(np.float32(1.0) / g32)
+        x = (p16 * inv).astype(np.float32)
+        c0 = F.e4m3_encode(x)
+        choices = [[int(c)] for c in c0]
+        for f in (1 - DELTA, 1 + DELTA):
+            c1 = F.e4m3_encode((x.astype(np.float64) * f).astype(np.float32))
+            for i in np.nonzero(c1 != c0)[0]:
+                if int(c1[i]) not in choices[i]:
+                    choices[i].append(int(c1[i]))
+        return [float(g32) * F.e4m3_value(np.array(c, dtype=np.uint8)) for c in itertools.product(*choices)]
     a = float(np.abs(p16).max())
     u = np.float32(np.float32(6.0) * g32)
     t = np.float32(np.float32(a) / u)
@@ -107,6 +118,102 @@ def _block_options(p16, g):
     return out
 
 
+def p_tie_rows(qh, kh, vh, row, softmax_scale, flags, g_p, causal, multipliers, limit=4096):
+    """Oracle output rows (one query row of one head) for every combination
+    of the P rounding decisions that lie within DELTA of a boundary, the
+    oracle's own row first; None if there are more than ``limit``."""
+    fp8 = bool(flags & P.FP8_P)
+    kw = dict(causal=causal, sparse_2_4=bool(flags & P.SPARSE_2_4), p_fp8=fp8, multipliers=multipliers)
+    opts = {}
+
+    def record(p32, t0):
+        res = np.empty(p32.shape)
+        for blk in range(p32.shape[1] // 16):
+            o = _block_options(p32[0, 16 * blk:16 * blk + 16], g_p, fp8)
+            res[0, 16 * blk:16 * blk + 16] = o[0]
+            if len(o) > 1:
+                opts[(t0, blk)] = o
+        return res
+
+    P.attend_rows(qh, kh, vh, [row], softmax_scale, True, g_p, record, **kw)
+    keys = sorted(opts)
+    n_comb = int(np.prod([len(opts[k]) for k in keys])) if keys else 1
+    if n_comb > limit:
+        return None
+    rows = []
+    for combo in itertools.product(*[range(len(opts[k])) for k in keys]):
+        pick = dict(zip(keys, combo))
+
+        def quant(p32, t0):
+            res = np.empty(p32.shape)
+            for blk in range(p32.shape[1] // 16):
+                o = _block_options(p32[0, 16 * blk:16 * blk + 16], g_p, fp8)
+                res[0, 16 * blk:16 * blk + 16] = o[pick[(t0, blk)]] if (t0, blk) in pick else o[0]
+            return res
+
+        rows.append(P.attend_rows(qh, kh, vh, [row], softmax_scale, True, g_p, quant, **kw))
+    return rows
+
+
+def sparse_tie_keeps(qh, kh, row, causal, multipliers, limit=64):
+    """2:4 choices for one query row: the oracle's own first, then those that
+    exchange the 2nd- and 3rd-ranked keys of any group whose two scores lie
+    within fp32 accumulation error of each other (2^-16 of the larger sum of
+    absolute products), which the GPU may order either way.  Each is a
+    ``keep_fn`` for ``attend_rows``; None if more than ``limit``."""
+    nk = row + 1 if causal else kh.shape[0]
+    n4 = (nk + 3) // 4 * 4
+    qr = qh[row] / multipliers[0]
+    kr = kh[:nk] / multipliers[1]
+    z = np.full(n4, -np.inf)
+    z[:nk] = kr @ qr
+    absd = np.zeros(n4)
+    absd[:nk] = np.abs(kr) @ np.abs(qr)
+    swaps = []
+    for g0 in range(0, n4, 4):
+        idx = [j for j in range(g0, g0 + 4) if j < nk]
+        if len(idx) < 3:
+            continue
+        order = sorted(idx, key=lambda j: (-z[j], j))
+        a, b = order[1], order[2]
+        if abs(z[a] - z[b]) <= 2.0 ** -16 * max(absd[a], absd[b]):
+            swaps.append((a, b))
+    if 2 ** len(swaps) > limit:
+        return None
+    fns = []
+    for pick in itertools.product([False, True], repeat=len(swaps)):
+        flips = [s for s, f in zip(swaps, pick) if f]
+
+        def keep(score, valid, flips=flips):
+            k = P.keep_2_4(score, valid)
+            for a, b in flips:
+                k[0, a], k[0, b] = k[0, b], k[0, a]
+            return k
+        fns.append(keep)
+    return fns
+
+
+def _row_explained_by_sparse_ties(inp, n, h, row, gs, gvals):
+    """Whether exchanging near-equal scores in the 2:4 choice (and no other
+    difference) makes the oracle's row quantize to the GPU's."""
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    a, b = int(cu[n]), int(cu[n + 1])
+    qh, kh, vh = P.quantize_operands(inp.q[a:b, [h]].float().numpy(), inp.k[a:b, [h]].float().numpy(),
+                                     inp.v[a:b, [h]].float().numpy(), [0, b - a], inp.flags,
+                                     inp.g_q, inp.g_k, inp.g_v)
+    mult = P.operand_multipliers(inp.flags, inp.g_q, inp.g_k)
+    fns = sparse_tie_keeps(qh[:, 0], kh[:, 0], row, True, mult)
+    if not fns or len(fns) == 1:
+        return False
+    for keep in fns[1:]:
+        o, _ = P.attend_rows(qh[:, 0], kh[:, 0], vh[:, 0], [row], inp.softmax_scale, bool(inp.flags & P.FLAG_P),
+                             inp.g_p, causal=True, sparse_2_4=True, p_fp8=bool(inp.flags & P.FP8_P),
+                             multipliers=mult, keep_fn=keep)
+        if _valid(o.astype(np.float32), gs[None], gvals[None], inp.g_out).all():
+            return True
+    return False
+
+
 def _row_explained_by_p_ties(inp, n, h, row, gs, gvals):
     """Whether some combination of near-boundary P rounding decisions makes
     the oracle's output row (sequence n, local row, head h) quantize to the
@@ -116,37 +223,11 @@ def _row_explained_by_p_ties(inp, n, h, row, gs, gvals):
     qh, kh, vh = P.quantize_operands(inp.q[a:b, [h]].float().numpy(), inp.k[a:b, [h]].float().numpy(),
                                      inp.v[a:b, [h]].float().numpy(), [0, b - a], inp.flags,
                                      inp.g_q, inp.g_k, inp.g_v)
-    opts = {}
-
-    def record(p32, t0):
-        res = np.empty(p32.shape)
-        for blk in range(p32.shape[1] // 16):
-            o = _block_options(p32[0, 16 * blk:16 * blk + 16], inp.g_p)
-            res[0, 16 * blk:16 * blk + 16] = o[0]
-            if len(o) > 1:
-                opts[(t0, blk)] = o
-        return res
-
-    o_ref, _ = P.attend_rows(qh[:, 0], kh[:, 0], vh[:, 0], [row], inp.softmax_scale, True, inp.g_p, record)
-    keys = sorted(opts)
-    n_comb = int(np.prod([len(opts[k]) for k in keys])) if keys else 1
-    if n_comb > 4096:
+    rows = p_tie_rows(qh[:, 0], kh[:, 0], vh[:, 0], row, inp.softmax_scale, inp.flags, inp.g_p, True,
+                      P.operand_multipliers(inp.flags, inp.g_q, inp.g_k))
+    if rows is None:
         return False
-    for combo in itertools.product(*[range(len(opts[k])) for k in keys]):
-        pick = dict(zip(keys, combo))
-
-        def quant(p32, t0):
-            res = np.empty(p32.shape)
-            for blk in range(p32.shape[1] // 16):
-                o = _block_options(p32[0, 16 * blk:16 * blk + 16], inp.g_p) if (t0, blk) in pick else None
-                res[0, 16 * blk:16 * blk + 16] = o[pick[(t0, blk)]] if o else \
-                    F.nvfp4_qdq(p32[:, 16 * blk:16 * blk + 16], inp.g_p, axis=-1)[0]
-            return res
-
-        o_row, _ = P.attend_rows(qh[:, 0], kh[:, 0], vh[:, 0], [row], inp.softmax_scale, True, inp.g_p, quant)
-        if _valid(o_row.astype(np.float32), gs[None], gvals[None], inp.g_out).all():
-            return True
-    return False
+    return any(_valid(o.astype(np.float32), gs[None], gvals[None], inp.g_out).all() for o, _ in rows)
 
 
 def _compare(inp, gpu, heads, rows_of, what):
@@ -190,6 +271,10 @@ def _compare(inp, gpu, heads, rows_of, what):
                 n = int(np.searchsorted(cu, t, side="right") - 1)
                 if inp.flags & P.FLAG_P and _row_explained_by_p_ties(inp, n, h, t - int(cu[n]), gs[r], gvals[r]):
                     print(f"    head {h} row {t}: explained by near-boundary P rounding", flush=True)
+                    bad[r] = False
+                elif inp.flags & P.SPARSE_2_4 and _row_explained_by_sparse_ties(inp, n, h, t - int(cu[n]), gs[r],
+                                                                                gvals[r]):
+                    print(f"    head {h} row {t}: explained by near-equal scores in the 2:4 choice", flush=True)
                     bad[r] = False
             n_invalid += int(bad.sum())
             for r, c in list(zip(*np.nonzero(bad)))[:5]:

@@ -1,0 +1,248 @@
+"""GPU parity of the prefill's operand formats and 2:4 sparsity (NVFP4
+output, same bars and validity checks as the NVFP4 prefill), of the fp32
+attention over a cached context and the causal attention it merges with, and
+of the chunked-prefill chain from the paged NVFP4 cache: gather, the model's
+projection (done here with torch), context and new-token attention, LSE merge,
+NVFP4 quantization.
+
+fp32 outputs: rel-L2 <= 2e-3 over the compared rows, LSE within 1e-3, and
+every row within max-abs 1e-2 of the oracle's, or of the oracle's row under
+some combination of P rounding decisions that lie within 2^-14 of a boundary
+(the GPU forms P in fp32 from fp32 scores).
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_attention_nvfp4_amd import ops, workloads
+from oracle import formats as F
+from oracle import prefill as P
+from oracle import record as R
+from oracle import swizzle as S
+from test_gpu_prefill import _compare, _run_gpu, p_tie_rows
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 2e-3
+MAX_ABS = 1e-2
+LSE_ABS = 1e-3
+
+FMT = [
+    # seed, lens, H, flags
+    (21, [1, 17, 64, 65, 130], 3, 255),            # Q, K, P, V per-tensor FP8
+    (22, [300, 0, 257, 31], 2, 15 | 32 | 64),      # K and P FP8, Q and V NVFP4
+    (23, [190, 64], 2, 4 | 64),                    # P FP8 only (bf16 PV products)
+    (24, [129, 250], 2, 1 | 16 | 8 | 128),         # Q and V FP8 only
+    (25, [200, 77, 5], 2, 15 | 256),               # NVFP4 Q/K/P/V with 2:4 sparsity
+    (26, [100, 300], 2, 255 | 256),                # FP8 Q/K/P/V with 2:4 sparsity
+    (27, [70, 131], 2, 3 | 256),                   # NVFP4 Q, K with 2:4 sparsity
+]
+
+
+@pytest.mark.parametrize("case", FMT, ids=[f"prefill{c[0]}-flags{c[3]}" for c in FMT])
+def test_prefill_formats_and_sparsity(case):
+    seed, lens, H, flags = case
+    inp = workloads.prefill_inputs(200 + seed, lens, H, flags)
+    print(f"  prefill seed={seed} lens={lens} H={H} flags={flags} T={inp.T}", flush=True)
+    _compare(inp, _run_gpu(inp), list(range(H)), None, f"prefill{seed}")
+
+
+GRID = [
+    (31, [1, 2, 3, 4, 5, 70, 133], 2, 256),        # 2:4 only: ties between equal scores everywhere
+    (32, [90, 33], 2, 256 | 12),                    # with P and V NVFP4 (fp16 PV products)
+    (33, [64, 129], 2, 256 | 4 | 64 | 8),           # with P FP8, V NVFP4
+]
+
+
+@pytest.mark.parametrize("case", GRID, ids=[f"grid{c[0]}-flags{c[3]}" for c in GRID])
+def test_prefill_sparsity_on_exact_scores(case):
+    """Q and K on a coarse grid: every score is exact in fp32, so the GPU's
+    2:4 choice must be the oracle's, ties included."""
+    seed, lens, H, flags = case
+    inp = workloads.grid_prefill_inputs(300 + seed, lens, H, flags)
+    _compare(inp, _run_gpu(inp), list(range(H)), None, f"grid{seed}")
+
+
+def test_prefill_workload_all_fp8_with_sparsity():
+    """The full prefill workload's shape (8 sequences of 2k-8k tokens, 128
+    heads) with every operand per-tensor FP8 and 2:4 sparsity; the oracle
+    checks heads 0 and 77 on the first, last and 32 random rows of each
+    sequence."""
+    base = workloads.prefill_workload()
+    lens = (base.cu_seqlens[1:] - base.cu_seqlens[:-1]).tolist()
+    inp = workloads.prefill_inputs(workloads.SEED_BASE + 4, lens, 128, 255 | 256, name="prefill4-fp8-2:4")
+    rng = np.random.default_rng(11)
+
+    def rows_of(n, L):
+        return np.unique(np.concatenate([np.arange(min(32, L)), np.arange(max(0, L - 32), L),
+                                         rng.integers(0, L, 32)]))
+
+    _compare(inp, _run_gpu(inp), [0, 77], rows_of, "prefill workload fp8 2:4")
+
+
+# --------------------------------------------------- fp32 attention --
+
+def _gpu_attention(q, k, v, cu_q, max_q, inp, flags, causal, cu_k=None, max_k=0, out=None, lse=None):
+    out, lse = ops.prefill_attention(q, k, v, cu_q, max_q, inp.softmax_scale, flags, inp.g_q, inp.g_k, inp.g_v,
+                                     inp.g_p, causal=causal, cu_seqlens_k=cu_k, max_seqlen_k=max_k, out=out, lse=lse)
+    return out, lse
+
+
+def _check_rows(got_o, got_l, ref_o, ref_l, alt_rows, what):
+    """fp32 bars; alt_rows(t, h) yields the oracle's alternative rows of
+    (token t, head h) for near-boundary P decisions (or nothing)."""
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), empty), f"{what}: -inf LSE pattern differs"
+    assert np.all(got_o[empty] == 0), f"{what}: rows without keys must be zero"
+    num = float(((got_o - ref_o) ** 2).sum())
+    den = float((ref_o ** 2).sum())
+    rel = np.sqrt(num / den) if den > 0 else np.sqrt(num)
+    lab = float(np.abs(got_l[~empty] - ref_l[~empty]).max()) if (~empty).any() else 0.0
+    err = np.abs(got_o - ref_o).max(axis=-1)
+    bad = np.argwhere(err > MAX_ABS)
+    unexplained = 0
+    for t, h in bad:
+        alts = alt_rows(int(t), int(h))
+        if not alts or not any(np.abs(got_o[t, h] - o[0]).max() <= MAX_ABS for o, _ in alts):
+            unexplained += 1
+    print(f"  {what}: rel_l2={rel:.3e} max_abs={float(err.max()) if err.size else 0:.3e} lse_abs={lab:.3e}; "
+          f"rows beyond max-abs {len(bad)}, unexplained {unexplained}", flush=True)
+    assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e}"
+    assert lab <= LSE_ABS, f"{what}: lse abs {lab:.3e}"
+    assert unexplained == 0, f"{what}: {unexplained} rows beyond max-abs {MAX_ABS} without a P-rounding explanation"
+
+
+CTX = [
+    # seed, new lens, context lens, H, flags
+    (41, [5, 40, 3], [100, 1, 0], 2, 0),
+    (42, [64, 17], [512, 300], 2, 11),            # Q, K, V NVFP4 (no P: schedule-free)
+    (43, [33, 1, 90], [257, 64, 1000], 2, 15),    # all four NVFP4
+    (44, [20, 70], [130, 600], 3, 255),           # all four FP8
+]
+
+
+@pytest.mark.parametrize("case", CTX, ids=[f"ctx{c[0]}-flags{c[4]}" for c in CTX])
+def test_context_attention(case):
+    """New tokens over their sequences' cached context (every key visible),
+    fp32 output and LSE."""
+    seed, new_lens, ctx_lens, H, flags = case
+    ci = workloads.context_inputs(400 + seed, new_lens, ctx_lens, H, flags)
+    inp = ci.new
+    out, lse = _gpu_attention(inp.q.cuda(), ci.ctx_k.cuda(), ci.ctx_v.cuda(), inp.cu_seqlens.cuda(), inp.max_seqlen,
+                              inp, flags, False, ci.cu_ctx.cuda(), ci.max_ctx)
+    torch.cuda.synchronize()
+    q, ck, cv = inp.q.float().numpy(), ci.ctx_k.float().numpy(), ci.ctx_v.float().numpy()
+    cq, cc = inp.cu_seqlens.numpy(), ci.cu_ctx.numpy()
+    ref_o, ref_l = P.attention(q, ck, cv, cq, cc, inp.softmax_scale, flags, inp.g_q, inp.g_k, inp.g_v, inp.g_p,
+                               False)
+    qh = P.quantize_q(q, flags, inp.g_q)
+    kh, vh = P.quantize_kv(ck, cv, cc, flags, inp.g_k, inp.g_v)
+    mult = P.operand_multipliers(flags, inp.g_q, inp.g_k)
+
+    def alt_rows(t, h):
+        if not flags & P.FLAG_P:
+            return []
+        n = int(np.searchsorted(cq, t, side="right") - 1)
+        a, ka, kb = int(cq[n]), int(cc[n]), int(cc[n + 1])
+        return p_tie_rows(qh[a:int(cq[n + 1]), h], kh[ka:kb, h], vh[ka:kb, h], t - a, inp.softmax_scale, flags,
+                          inp.g_p, False, mult) or []
+
+    _check_rows(out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_l, alt_rows, f"ctx{seed}")
+
+
+def test_causal_attention_fp32_output_matches_fused_path():
+    """The causal fp32-output attention is the same computation as the fused
+    NVFP4 prefill: quantizing its rows gives the fused path's codes, scales
+    and LSE bit for bit (one kernel template, two epilogues)."""
+    inp = workloads.prefill_inputs(451, [300, 65, 1], 2, 15)
+    codes, scales, lse_f = _run_gpu(inp)
+    out, lse = _gpu_attention(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.cu_seqlens.cuda(), inp.max_seqlen, inp,
+                              inp.flags, True)
+    c2, s2 = ops.quantize_rows(out.reshape(inp.T, -1), inp.g_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy().reshape(codes.shape), codes)
+    assert np.array_equal(s2.cpu().numpy()[:scales.size], scales)
+    assert np.array_equal(lse.cpu().double().numpy(), lse_f)
+
+
+# --------------------------------------------------- chunked prefill --
+
+def _cache_from_context(seed, ctx_lens, rec=432):
+    d = workloads.small_decode(seed, len(ctx_lens), 1, ctx_lens, page_size=64, rec=rec, outer=1.3)
+    cache = torch.zeros((d.num_pages, d.page_size, d.record_bytes), dtype=torch.uint8, device="cuda")
+    ops.cache_write(d.kv_c.cuda(), d.k_pe.cuda(), d.slot_mapping.cuda(), cache, d.outer_scale)
+    return d, cache
+
+
+@pytest.mark.parametrize("rec", [432, 368])
+def test_cache_gather_bit_exact(rec):
+    d, cache = _cache_from_context(460 + rec, [200, 0, 64, 131], rec)
+    lens = d.seq_lens.tolist()
+    starts = torch.tensor([5, 0, 0, 64], dtype=torch.int32)
+    cnt = [max(0, L - int(s)) for L, s in zip(lens, starts.tolist())]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(cnt)]), dtype=torch.int32)
+    kv, pe = ops.cache_gather(cache, d.page_table.cuda(), cu.cuda(), max(cnt), d.outer_scale, starts.cuda())
+    torch.cuda.synchronize()
+    flat = cache.view(-1, rec).cpu().numpy()
+    pt = d.page_table.numpy()
+    for n in range(len(lens)):
+        pos = np.arange(int(starts[n]), lens[n])
+        slots = pt[n][pos // 64] * 64 + pos % 64 if pos.size else np.zeros(0, np.int64)
+        want_kv, want_pe = R.gather_bf16(flat[slots], d.outer_scale)
+        got_kv = kv[int(cu[n]):int(cu[n + 1])].view(torch.int16).cpu().numpy().view(np.uint16)
+        got_pe = pe[int(cu[n]):int(cu[n + 1])].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_kv, want_kv) and np.array_equal(got_pe, want_pe), f"sequence {n}"
+
+
+@pytest.mark.parametrize("flags", [11, 15], ids=["flags11", "flags15"])
+def test_chunked_prefill_chain(flags):
+    """A chunk of new tokens over the cached context of each sequence: gather
+    the context from the paged NVFP4 cache, project it (the model's kv_b_proj,
+    random bf16 weights, torch here), attend (context and causal new-token
+    parts into one [T, 2, H, 128] buffer), merge by LSE, quantize to NVFP4.
+    The merged rows against the oracle's chunked prefill on the same
+    projected operands; the NVFP4 codes against the oracle's quantizer on the
+    GPU's merged rows, bit for bit."""
+    H = 2
+    ctx_lens, new_lens = [300, 70, 0], [40, 5, 33]
+    d, cache = _cache_from_context(470 + flags, ctx_lens)
+    cu_ctx = torch.tensor(np.concatenate([[0], np.cumsum(ctx_lens)]), dtype=torch.int32)
+    kv, pe = ops.cache_gather(cache, d.page_table.cuda(), cu_ctx.cuda(), max(ctx_lens), d.outer_scale)
+    g = torch.Generator().manual_seed(471)
+    w_uk = (torch.randn((512, H * 128), generator=g) / 512 ** 0.5).to(torch.bfloat16).cuda()
+    w_uv = (torch.randn((512, H * 128), generator=g) / 512 ** 0.5).to(torch.bfloat16).cuda()
+    Tc = int(cu_ctx[-1])
+    k_nope = (kv.float() @ w_uk.float()).to(torch.bfloat16).view(Tc, H, 128)
+    ctx_k = torch.cat([k_nope, pe.view(Tc, 1, 64).expand(Tc, H, 64)], dim=2).contiguous()
+    ctx_v = (kv.float() @ w_uv.float()).to(torch.bfloat16).view(Tc, H, 128).contiguous()
+    inp = workloads.prefill_inputs(472 + flags, new_lens, H, flags)
+    amax = lambda *ts: max(float(t.abs().max()) for t in ts)
+    inp.g_k = float(np.float32(amax(inp.k, ctx_k) / 2688))
+    inp.g_v = inp.g_out = float(np.float32(amax(inp.v, ctx_v) / 2688))
+    T = inp.T
+    part_o = torch.empty((T, 2, H, 128), dtype=torch.float32, device="cuda")
+    part_l = torch.empty((T, 2, H), dtype=torch.float32, device="cuda")
+    cu_q = inp.cu_seqlens.cuda()
+    _gpu_attention(inp.q.cuda(), ctx_k, ctx_v, cu_q, inp.max_seqlen, inp, flags, False, cu_ctx.cuda(), max(ctx_lens),
+                   out=part_o[:, 0], lse=part_l[:, 0])
+    _gpu_attention(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), cu_q, inp.max_seqlen, inp, flags, True,
+                   out=part_o[:, 1], lse=part_l[:, 1])
+    out, lse = ops.lse_merge(part_o, part_l)
+    codes, scales = ops.quantize_rows(out.reshape(T, -1), inp.g_out)
+    torch.cuda.synchronize()
+    ref_o, ref_l = P.chunked_prefill(inp.q.float().numpy(), inp.k.float().numpy(), inp.v.float().numpy(),
+                                     inp.cu_seqlens.numpy(), ctx_k.float().cpu().numpy(), ctx_v.float().cpu().numpy(),
+                                     cu_ctx.numpy(), inp.softmax_scale, flags, inp.g_q, inp.g_k, inp.g_v, inp.g_p)
+    got_o = out.cpu().double().numpy()
+    got_l = lse.cpu().double().numpy()
+    num = float(((got_o - ref_o) ** 2).sum())
+    rel = np.sqrt(num / float((ref_o ** 2).sum()))
+    lab = float(np.abs(got_l - ref_l).max())
+    print(f"  chunked prefill flags={flags}: rel_l2={rel:.3e} max_abs={float(np.abs(got_o - ref_o).max()):.3e} "
+          f"lse_abs={lab:.3e}", flush=True)
+    assert rel <= REL_L2 and lab <= LSE_ABS
+    if not flags & P.FLAG_P:
+        assert float(np.abs(got_o - ref_o).max()) <= MAX_ABS
+    want_codes, want_scales = S.quantize_rows(out.reshape(T, -1).cpu().numpy(), inp.g_out)
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
