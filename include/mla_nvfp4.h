@@ -57,6 +57,8 @@ typedef enum {
 #define MLA_D_ROPE 64
 #define MLA_RECORD_BYTES_BF16_ROPE 432
 #define MLA_RECORD_BYTES_FP8_ROPE 368
+/* Raw (unquantized) latent record of mla_decode_qdq: 512 + 64 bf16 values. */
+#define MLA_RAW_RECORD_BYTES 1152
 /* Prefill head dims ([MO-MLA], commit 1: asymmetric 192/128 head dims). */
 #define MLA_PREFILL_D_QK 192
 #define MLA_PREFILL_D_V 128
@@ -239,6 +241,55 @@ int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope,
                             const int32_t* indices, int topk, int max_splits,
                             void* workspace, size_t workspace_bytes,
                             float* out, float* lse, void* stream);
+
+/* Dense decode with quantized attention operands.  [MO-MLA], PR body and
+ * commit 4: every attention matmul operand is fake-quantized once along its
+ * own contraction axis; the split-K decode quantizes P after the softmax row
+ * sum (the denominator unquantized), takes the caller's Q in an FP32
+ * carrier (the dequantized values are used as they are), and, with a raw
+ * latent cache, quantizes K along the feature axis and V along the token
+ * axis, V in blocks of 16 at absolute token positions.
+ *
+ * Arguments as mla_decode_nvfp4, plus qdq_flags (the MLA_QDQ_* bits of the
+ * prefill: Q, K, P, V and their FP8 format bits) and the multipliers g_q,
+ * g_k, g_v, g_p (used for enabled operands; finite, > 0).
+ *  record_bytes 432 or 368: NVFP4 records; K and V are the stored latent
+ *               (times outer_scale); the K and V flags are refused (the
+ *               latent is already quantized once).
+ *  record_bytes MLA_RAW_RECORD_BYTES (1152): raw records (mla_raw_cache_write:
+ *               512 bf16 latent then 64 bf16 RoPE values); outer_scale unused.
+ *               K = [latent, RoPE] quantized along its 576 features (36 NVFP4
+ *               blocks of 16, or per-tensor FP8) with g_k when MLA_QDQ_K;
+ *               V = latent quantized along tokens with g_v when MLA_QDQ_V:
+ *               NVFP4 blocks [16k, 16k+16) of positions < L per dim (the last
+ *               one open), or per-tensor FP8.
+ * Q (576-d) is quantized along its features like K.  Schedule: the tokens
+ * of each split-K chunk (mla_decode_num_splits) are taken in tiles of 32
+ * from the chunk start with a running max refreshed per tile; P is quantized
+ * against it: NVFP4 16-key blocks aligned to the tile (keys past L count as
+ * zeros), or per-tensor FP8.  Chunks merge by LSE in chunk order.
+ *  workspace  >= mla_decode_workspace_bytes(B, H, max_splits) (max_splits > 1)
+ * Dense only (no top-k form). */
+int mla_decode_qdq(const uint16_t* q_nope, const uint16_t* q_rope,
+                   int64_t q_stride_b, int64_t q_stride_h,
+                   const uint8_t* cache, int64_t num_pages, int record_bytes,
+                   int page_size, const int32_t* page_table, int max_pages_per_seq,
+                   const int32_t* seq_lens, int B, int H,
+                   float outer_scale, float softmax_scale, unsigned qdq_flags,
+                   float g_q, float g_k, float g_v, float g_p, int max_splits,
+                   void* workspace, size_t workspace_bytes,
+                   float* out, float* lse, void* stream);
+
+/* Write T tokens into a raw latent cache (records of MLA_RAW_RECORD_BYTES:
+ * the 512 bf16 kv_c values, then the 64 bf16 k_pe values), the cache whose
+ * K and V mla_decode_qdq quantizes on read ([MO-MLA], commit 4: the latent
+ * cache stays raw in that model).  kv_c, k_pe: bf16 rows with strides
+ * (multiples of 8, 16-byte aligned); a slot < 0 or >= num_slots skips the
+ * token.  T == 0 is a no-op. */
+int mla_raw_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride,
+                        const uint16_t* k_pe, int64_t k_pe_row_stride,
+                        const int64_t* slot_mapping, int64_t T,
+                        uint8_t* cache, int64_t num_slots, void* stream);
 
 /* Merge S partial attention results over disjoint token sets.  [MO-MLA],
  * commit 1: partials carry a natural-log LSE so that chunks can be merged.  For each (b, h)

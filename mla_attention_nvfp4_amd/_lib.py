@@ -33,6 +33,9 @@ SIGNATURES = {
     "mla_sparse_decode_nvfp4": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p,
                                         c_int, c_int, c_f32, c_f32, c_p, c_int, c_int, c_p, c_sz, c_p, c_p,
                                         c_p]),
+    "mla_decode_qdq": (c_int, [c_p, c_p, c_i64, c_i64, c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_int, c_int,
+                               c_f32, c_f32, c_u32, c_f32, c_f32, c_f32, c_f32, c_int, c_p, c_sz, c_p, c_p, c_p]),
+    "mla_raw_cache_write": (c_int, [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p]),
     "mla_lse_merge": (c_int, [c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_p, c_p, c_p]),
     "mla_prefill_workspace_bytes": (c_sz, [c_i64, c_int, c_u32]),
     "mla_prefill_nvfp4_out": (c_int, [c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_int,
@@ -218,6 +221,43 @@ def sparse_decode(q_nope, q_rope, cache, page_table, seq_lens, indices, outer_sc
         cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
         seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), indices.data_ptr(),
         indices.shape[1], int(max_splits), _ptr(ws), 0 if ws is None else ws.numel(), out.data_ptr(),
+        lse.data_ptr(), _stream(q_nope)))
+    return out, lse
+
+
+RAW_RECORD_BYTES = 1152
+
+
+def raw_cache_write(kv_c, k_pe, slot_mapping, cache) -> None:
+    """kv_c bf16 [T,512], k_pe bf16 [T,64] (row-strided), slot_mapping int64 [T],
+    cache uint8 [..., 1152] contiguous (raw records)."""
+    _need(kv_c, torch.bfloat16, "kv_c")
+    _need(k_pe, torch.bfloat16, "k_pe")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(cache, torch.uint8, "cache")
+    if kv_c.dim() != 2 or kv_c.shape[1] != 512 or kv_c.stride(1) != 1 or k_pe.dim() != 2 or k_pe.shape[1] != 64 \
+            or k_pe.stride(1) != 1 or k_pe.shape[0] != kv_c.shape[0]:
+        raise ValueError("kv_c [T, 512] and k_pe [T, 64] with unit inner stride")
+    if not cache.is_contiguous() or cache.shape[-1] != RAW_RECORD_BYTES or slot_mapping.numel() != kv_c.shape[0]:
+        raise ValueError("cache must be contiguous [..., 1152] and slot_mapping [T]")
+    _check(lib().mla_raw_cache_write(kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0),
+                                     slot_mapping.data_ptr(), kv_c.shape[0], cache.data_ptr(), cache.numel() // 1152,
+                                     _stream(cache)))
+
+
+def decode_qdq(q_nope, q_rope, cache, page_table, seq_lens, outer_scale, softmax_scale, flags, g_q=1.0, g_k=1.0,
+               g_v=1.0, g_p=1.0, max_splits=1, out=None, lse=None, workspace=None):
+    """Dense paged decode with quantized operands (NVFP4 or raw records)."""
+    _decode_common(q_nope, q_rope, cache, page_table, seq_lens)
+    B, H = q_nope.shape[:2]
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=q_nope.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device) if lse is None else lse
+    ws = _workspace(B, H, max_splits, q_nope, workspace)
+    _check(lib().mla_decode_qdq(
+        q_nope.data_ptr(), q_rope.data_ptr(), q_nope.stride(0), q_nope.stride(1), cache.data_ptr(),
+        cache.shape[0], cache.shape[2], cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+        seq_lens.data_ptr(), B, H, float(outer_scale), float(softmax_scale), int(flags), float(g_q), float(g_k),
+        float(g_v), float(g_p), int(max_splits), _ptr(ws), 0 if ws is None else ws.numel(), out.data_ptr(),
         lse.data_ptr(), _stream(q_nope)))
     return out, lse
 

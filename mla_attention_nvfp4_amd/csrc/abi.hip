@@ -82,8 +82,8 @@ int check_decode(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_strid
                  const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
                  const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
                  float outer_scale, float softmax_scale, int max_splits, void* workspace,
-                 size_t workspace_bytes, float* out, float* lse) {
-    int rc = check_record(record_bytes);
+                 size_t workspace_bytes, float* out, float* lse, bool raw_ok = false) {
+    int rc = (raw_ok && record_bytes == MLA_RAW_RECORD_BYTES) ? MLA_OK : check_record(record_bytes);
     if (rc) return rc;
     if (B < 0 || B > 65535 || H < 1 || H > 4096)
         return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= B <= 65535 and 1 <= H <= 4096 (B=%d H=%d)", B, H);
@@ -220,6 +220,82 @@ size_t mla_decode_workspace_bytes(int B, int H, int max_splits) {
 }
 
 int mla_prefill_p_tile(void) { return mla::prefill_p_tile(); }
+
+int mla_raw_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride, const uint16_t* k_pe, int64_t k_pe_row_stride,
+                        const int64_t* slot_mapping, int64_t T, uint8_t* cache, int64_t num_slots, void* stream) {
+    if (T < 0 || num_slots < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "T and num_slots must be >= 0");
+    if (T > (int64_t)INT32_MAX * 4) return fail(MLA_ERR_INVALID_ARGUMENT, "T too large");
+    if (T == 0) return ok();
+    if (!kv_c || !k_pe || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (kv_c_row_stride % 8 || k_pe_row_stride % 8 || kv_c_row_stride < MLA_D_LATENT || k_pe_row_stride < MLA_D_ROPE ||
+        !aligned(kv_c, 16) || !aligned(k_pe, 16) || !aligned(cache, 16))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "kv_c / k_pe rows must be 16-byte aligned with strides >= 512 / 64 "
+                    "(multiples of 8), and the cache 16-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_raw_cache_write(kv_c, kv_c_row_stride, k_pe, k_pe_row_stride, slot_mapping, T, cache,
+                                                  num_slots, static_cast<hipStream_t>(stream)),
+                      "raw cache write launch");
+}
+
+int mla_decode_qdq(const uint16_t* q_nope, const uint16_t* q_rope, int64_t q_stride_b, int64_t q_stride_h,
+                   const uint8_t* cache, int64_t num_pages, int record_bytes, int page_size,
+                   const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int B, int H,
+                   float outer_scale, float softmax_scale, unsigned qdq_flags, float g_q, float g_k, float g_v,
+                   float g_p, int max_splits, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                   void* stream) {
+    int rc = check_decode(q_nope, q_rope, q_stride_b, q_stride_h, cache, num_pages, record_bytes, page_size,
+                          page_table, max_pages_per_seq, seq_lens, B, H, outer_scale, softmax_scale, max_splits,
+                          workspace, workspace_bytes, out, lse, true);
+    if (rc) return rc;
+    if (qdq_flags & ~0xFFu) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown qdq_flags bits 0x%x", qdq_flags & ~0xFFu);
+    if ((qdq_flags & MLA_QDQ_FP8_MASK) >> 4 & ~qdq_flags & 0xFu)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "qdq_flags 0x%x: an FP8 format bit is set for an operand that is not "
+                    "quantized", qdq_flags);
+    if ((qdq_flags & (MLA_QDQ_K | MLA_QDQ_V)) && record_bytes != MLA_RAW_RECORD_BYTES)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "K and V are quantized on read only from raw (%d-byte) records; NVFP4 "
+                    "records already hold the quantized latent", MLA_RAW_RECORD_BYTES);
+    if (((qdq_flags & MLA_QDQ_Q) && !finite_pos(g_q)) || ((qdq_flags & MLA_QDQ_K) && !finite_pos(g_k)) ||
+        ((qdq_flags & MLA_QDQ_V) && !finite_pos(g_v)) || ((qdq_flags & MLA_QDQ_P) && !finite_pos(g_p)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "the scale of every enabled quantizer must be finite and > 0");
+    if (((qdq_flags & MLA_QDQ_FP8_Q) && !std::isfinite(1.0f / g_q)) || ((qdq_flags & MLA_QDQ_FP8_K) && !std::isfinite(1.0f / g_k)) ||
+        ((qdq_flags & MLA_QDQ_FP8_V) && !std::isfinite(1.0f / g_v)) || ((qdq_flags & MLA_QDQ_FP8_P) && !std::isfinite(1.0f / g_p)))
+        return fail(MLA_ERR_INVALID_ARGUMENT, "a per-tensor FP8 multiplier is too small (1/g overflows)");
+    if (B == 0) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    mla::DecodeArgs a{};
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.q_stride_b = q_stride_b;
+    a.q_stride_h = q_stride_h;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.record_bytes = record_bytes;
+    a.page_size = page_size;
+    a.page_recip = mla::page_recip_of(page_size);
+    a.page_table = page_table;
+    a.max_pages = max_pages_per_seq;
+    a.seq_lens = seq_lens;
+    a.indices = nullptr;
+    a.topk = 0;
+    a.B = B;
+    a.H = H;
+    a.outer_scale = outer_scale;
+    a.softmax_scale = softmax_scale;
+    a.max_splits = max_splits;
+    a.out = out;
+    a.lse = lse;
+    if (max_splits > 1) {
+        char* ws = static_cast<char*>(workspace);
+        a.ws_out = reinterpret_cast<float*>(ws);
+        a.ws_lse = reinterpret_cast<float*>(ws + decode_ws_out_bytes(B, H, max_splits));
+        a.ws_fmt = reinterpret_cast<uint8_t*>(ws + decode_ws_out_bytes(B, H, max_splits) +
+                                              decode_ws_lse_bytes(B, H, max_splits));
+    }
+    return hip_status(mla::launch_decode_qdq(a, qdq_flags, g_q, g_k, g_v, g_p, static_cast<hipStream_t>(stream)),
+                      "quantized-operand decode launch");
+}
 
 size_t mla_nvfp4_swizzled_scale_bytes(int64_t rows, int64_t scale_cols) {
     if (rows <= 0 || scale_cols <= 0) return 0;

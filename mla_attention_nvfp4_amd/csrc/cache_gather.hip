@@ -85,3 +85,37 @@ hipError_t launch_cache_gather(const uint8_t* cache, int64_t num_pages, bool rop
 }
 
 }  // namespace mla
+
+// Raw latent cache write: record = the token's 512 bf16 latent values then
+// its 64 bf16 RoPE values (1152 bytes), the cache that decode_qdq_kernel
+// quantizes on read.  One wavefront per token: 64 lanes x 16 bytes of
+// latent, lanes 0..7 x 16 bytes of RoPE.
+namespace mla {
+namespace {
+
+__global__ __launch_bounds__(256) void raw_cache_write_kernel(const uint16_t* __restrict__ kv, int64_t kv_stride,
+                                                              const uint16_t* __restrict__ pe, int64_t pe_stride,
+                                                              const int64_t* __restrict__ slots, int64_t T,
+                                                              uint8_t* __restrict__ cache, int64_t num_slots) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) return;
+    uint8_t* rec = cache + slot * 1152;
+    *reinterpret_cast<u32x4*>(rec + 16 * lane) = *reinterpret_cast<const u32x4*>(kv + t * kv_stride + 8 * lane);
+    if (lane < 8)
+        *reinterpret_cast<u32x4*>(rec + 1024 + 16 * lane) = *reinterpret_cast<const u32x4*>(pe + t * pe_stride + 8 * lane);
+}
+
+}  // namespace
+
+hipError_t launch_raw_cache_write(const uint16_t* kv_c, int64_t kv_stride, const uint16_t* k_pe, int64_t pe_stride,
+                                  const int64_t* slot_mapping, int64_t T, uint8_t* cache, int64_t num_slots,
+                                  hipStream_t stream) {
+    hipLaunchKernelGGL(raw_cache_write_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, kv_c, kv_stride,
+                       k_pe, pe_stride, slot_mapping, T, cache, num_slots);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -730,15 +730,19 @@ hipError_t launch_decode_w(const DecodeArgs& a, hipStream_t stream) {
 // Up to 16 heads: the narrow kernel (each wavefront its own tokens); more:
 // 128 heads per workgroup.  Split sequences are then merged by
 // split_merge_kernel.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    const hipError_t e = a.H <= 16 ? launch_decode_narrow(a, stream) : launch_decode_w<8>(a, stream);
-    if (e != hipSuccess || a.max_splits <= 1) return e;
+hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream) {
     const int64_t waves = (int64_t)a.B * a.H;
     if (a.indices)
         hipLaunchKernelGGL((split_merge_kernel<true>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((split_merge_kernel<false>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    const hipError_t e = a.H <= 16 ? launch_decode_narrow(a, stream) : launch_decode_w<8>(a, stream);
+    if (e != hipSuccess || a.max_splits <= 1) return e;
+    return launch_split_merge(a, stream);
 }
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {

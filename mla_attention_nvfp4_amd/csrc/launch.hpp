@@ -47,6 +47,16 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_narrow(const DecodeArgs& a, hipStream_t stream);   // H <= 16
+// Merge of a decode launch's split partials (after the decode kernel).
+hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream);
+// Decode with quantized operands (dense; record_bytes 432, 368 or 1152 raw).
+// flags: 1 Q, 2 K, 4 P, 8 V quantized; 16/32/64/128 the same as per-tensor FP8.
+hipError_t launch_decode_qdq(const DecodeArgs& a, unsigned flags, float g_q, float g_k, float g_v, float g_p,
+                             hipStream_t stream);
+// Raw (bf16) latent cache records: kv_c then k_pe, 1152 bytes.
+hipError_t launch_raw_cache_write(const uint16_t* kv_c, int64_t kv_stride, const uint16_t* k_pe, int64_t pe_stride,
+                                  const int64_t* slot_mapping, int64_t T, uint8_t* cache, int64_t num_slots,
+                                  hipStream_t stream);
 
 // n = splits_per_seq[b] clamped to [0, S], or S if the pointer is null.
 struct MergeArgs {

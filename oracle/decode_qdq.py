@@ -114,8 +114,10 @@ def operands(cache, page_table_row, page_size, L, outer_scale, flags, g_k, g_v):
     return k, v
 
 
-def _chunk(qh, k, v, z, a, b, flags, g_p):
-    """Step 4 over tokens [a, b) of one head's row: (out, lse)."""
+def _chunk(k, v, z, a, b, flags, g_p, p_quantizer=None):
+    """Step 4 over tokens [a, b) of one head's row: (out, lse).
+    ``p_quantizer(p32, t0)``, if given, replaces the P QDQ of the tile at
+    token t0 (a test hook for P decisions that lie on a rounding boundary)."""
     m, l = -np.inf, 0.0
     acc = np.zeros(D_LATENT)
     for t0 in range(a, b, TILE):
@@ -126,7 +128,9 @@ def _chunk(qh, k, v, z, a, b, flags, g_p):
         alpha = 0.0 if m == -np.inf else np.exp(m - m_new)
         p = np.where(np.isneginf(zt), 0.0, np.exp(zt - m_new))
         l = alpha * l + p.sum()
-        if flags & FLAG_P:
+        if flags & FLAG_P and p_quantizer is not None:
+            p_hat = p_quantizer(p.astype(F32), t0)
+        elif flags & FLAG_P:
             p32 = p.astype(F32)
             p_hat = fp8_qdq(p32, g_p) if flags & FP8_P else nvfp4_qdq(p32, g_p)
         else:
@@ -141,10 +145,11 @@ def _chunk(qh, k, v, z, a, b, flags, g_p):
 
 
 def decode_qdq(q_nope, q_rope, cache, page_table, seq_lens, page_size, outer_scale, softmax_scale,
-               flags, g_q, g_k, g_v, g_p, max_splits, batch=None):
+               flags, g_q, g_k, g_v, g_p, max_splits, batch=None, p_quantizer=None):
     """out [B,H,512], lse [B,H] (float64); ``batch`` restricts the work to a
     subset of sequences (other rows NaN).  ``cache`` is [pages, page_size,
-    record] with NVFP4 (432 / 368 B) or raw (1152 B) records."""
+    record] with NVFP4 (432 / 368 B) or raw (1152 B) records.
+    ``p_quantizer``: see ``_chunk``."""
     q = np.concatenate([np.asarray(q_nope, np.float64), np.asarray(q_rope, np.float64)], axis=-1)
     B, H = q.shape[:2]
     out = np.full((B, H, D_LATENT), np.nan)
@@ -156,7 +161,7 @@ def decode_qdq(q_nope, q_rope, cache, page_table, seq_lens, page_size, outer_sca
         z = float(softmax_scale) * (qh @ k.T)                          # [H, L]
         bounds = split_bounds(L, max_splits)
         for h in range(H):
-            parts = [_chunk(qh[h], k, v, z[h], a, e, flags, g_p) for a, e in zip(bounds[:-1], bounds[1:])]
+            parts = [_chunk(k, v, z[h], a, e, flags, g_p, p_quantizer) for a, e in zip(bounds[:-1], bounds[1:])]
             po = np.stack([o for o, _ in parts])
             pl = np.array([s for _, s in parts])
             out[b, h], lse[b, h] = lse_merge(po, pl)

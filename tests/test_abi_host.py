@@ -105,3 +105,22 @@ def test_noalloc_decode_refuses_requests_beyond_its_scratch():
     args = _decode_args(rec=400)
     del args[16:18]
     assert lib.mla_decode_nvfp4_noalloc(*args) == -2
+
+
+def test_quantized_operand_decode_and_raw_cache_reject_invalid_arguments():
+    lib = L.lib()
+    a = _decode_args()
+    head, tail = a[:15], a[15:]          # ... softmax_scale | max_splits, ws, wsb, out, lse, stream
+
+    def qdq(rec=432, flags=0, g=(1.0, 1.0, 1.0, 1.0)):
+        h = list(head)
+        h[6] = rec
+        return lib.mla_decode_qdq(*h, flags, *g, *tail)
+    assert qdq(rec=400) == -2
+    assert qdq(rec=432, flags=2) == -1            # K on read needs raw records
+    assert qdq(rec=1152, flags=16) == -1          # FP8 bit without its operand
+    assert qdq(rec=1152, flags=4, g=(1.0, 1.0, 1.0, 0.0)) == -1
+    assert qdq(rec=1152, flags=1 << 9) == -1
+    # raw cache write: misaligned rows
+    assert lib.mla_raw_cache_write(1 << 20, 513, 1 << 20, 64, 1 << 20, 4, 1 << 20, 8, None) == -1
+    assert lib.mla_raw_cache_write(None, 512, None, 64, None, 0, None, 0, None) == 0
