@@ -196,23 +196,36 @@ def bench_cache_write(inp, steps: int, warmup: int) -> dict:
 
 def bench_lse_merge(steps: int, warmup: int) -> dict:
     """mla_lse_merge on the dense decode shape: B=64 sequences, 4 splits, 128
-    heads, 512-d fp32 partials (the stand-alone merge entry point)."""
+    heads, 512-d fp32 partials (the stand-alone merge entry point), the input
+    rotated over 4 copies (268 MB, above the 256 MB Infinity Cache)."""
     B, S, H, D = 64, 4, 128, 512
     g = torch.Generator().manual_seed(4321)
-    po = torch.randn((B, S, H, D), generator=g).cuda()
-    pl = (torch.randn((B, S, H), generator=g) * 3).cuda()
+    po = [torch.randn((B, S, H, D), generator=g).cuda() for _ in range(4)]
+    pl = [(torch.randn((B, S, H), generator=g) * 3).cuda() for _ in range(4)]
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    ms = timed(lambda: ops.lse_merge(po, pl, out=out, lse=lse), steps, warmup)
+    it = [0]
+
+    def run():
+        r = it[0] % 4
+        it[0] += 1
+        ops.lse_merge(po[r], pl[r], out=out, lse=lse)
+
+    ms = timed(run, steps, warmup)
     nbytes = B * S * H * (D + 1) * 4 + B * H * (D + 1) * 4
     return {"kernel_us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9,
-            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": nbytes}
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": nbytes,
+            "note": "input rotated over 4 copies (268 MB)"}
 
 
-def bench_prefill(steps: int, warmup: int) -> dict:
+def bench_prefill(steps: int, warmup: int, flags: int | None = None) -> dict:
     """Varlen causal prefill, 8 sequences of 2k-8k tokens, 128 heads, all four
-    operand quantizers, NVFP4 output with swizzled scales and LSE."""
+    operand quantizers (NVFP4, or the given flags: FP8 formats, 2:4
+    sparsity), NVFP4 output with swizzled scales and LSE."""
     inp = workloads.prefill_workload()
+    if flags is not None:
+        lens = (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1]).tolist()
+        inp = workloads.prefill_inputs(workloads.SEED_BASE + 4, lens, 128, flags, name=f"prefill4-{flags}")
     dev = "cuda"
     q, k, v, cu = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.cu_seqlens.to(dev)
     T, H = inp.T, inp.H
@@ -230,9 +243,117 @@ def bench_prefill(steps: int, warmup: int) -> dict:
     flops = float(sum(H * 320 * L * (L + 1) for L in lens))
     p_elems = float(sum(H * L * (L + 1) // 2 for L in lens))
     nbytes = T * H * (192 * 2 * 2 + 128 * 2) + T * H * 64 + scales.numel() + T * H * 4
-    return {"tokens": T, "seq_lens": lens, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+    return {"tokens": T, "flags": inp.flags, "seq_lens": lens, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "frac_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
             "p_elements_per_s": p_elems / (ms * 1e-3), "gbps": nbytes / (ms * 1e-3) / 1e9}
+
+
+def bench_chunked_prefill(steps: int, warmup: int) -> dict:
+    """A chunk of 512 new tokens for each of 8 sequences holding 4096 cached
+    tokens (paged NVFP4 cache, 432-byte records), 128 heads, Q/K/P/V NVFP4:
+    gather of the 32,768 context tokens to bf16, context attention and causal
+    new-token attention (fp32 rows + LSE into one [T, 2, H, 128] buffer), LSE
+    merge, NVFP4 quantization of the merged rows.  The projection of the
+    gathered latent (the model's kv_b_proj) is done once beforehand with torch
+    and is not timed; it belongs to the model, not to this path."""
+    N, C, Tn, H = 8, 4096, 512, 128
+    d = workloads.small_decode(4100, N, 1, [C] * N, page_size=64, rec=432, outer=1.3)
+    dev = "cuda"
+    cache = torch.zeros((d.num_pages, d.page_size, d.record_bytes), dtype=torch.uint8, device=dev)
+    ops.cache_write(d.kv_c.to(dev), d.k_pe.to(dev), d.slot_mapping.to(dev), cache, d.outer_scale)
+    pt = d.page_table.to(dev)
+    cu_ctx = torch.arange(0, (N + 1) * C, C, dtype=torch.int32, device=dev)
+    kv, pe = ops.cache_gather(cache, pt, cu_ctx, C, d.outer_scale)
+    g = torch.Generator().manual_seed(4101)
+    w_uk = (torch.randn((512, H * 128), generator=g) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+    w_uv = (torch.randn((512, H * 128), generator=g) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+    Tc = N * C
+    ctx_k = torch.cat([(kv.float() @ w_uk.float()).to(torch.bfloat16).view(Tc, H, 128),
+                       pe.view(Tc, 1, 64).expand(Tc, H, 64)], dim=2).contiguous()
+    ctx_v = (kv.float() @ w_uv.float()).to(torch.bfloat16).view(Tc, H, 128).contiguous()
+    inp = workloads.prefill_inputs(4102, [Tn] * N, H, 15)
+    q, k, v, cu_q = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.cu_seqlens.to(dev)
+    T = inp.T
+    part_o = torch.empty((T, 2, H, 128), dtype=torch.float32, device=dev)
+    part_l = torch.empty((T, 2, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_c = torch.empty(ops.prefill_workspace_bytes(Tc, H, 15), dtype=torch.uint8, device=dev)
+    ws_n = torch.empty(ops.prefill_workspace_bytes(T, H, 15), dtype=torch.uint8, device=dev)
+    a = (inp.softmax_scale, 15, inp.g_q, inp.g_k, inp.g_v, inp.g_p)
+    stages = {
+        "gather": lambda: ops.cache_gather(cache, pt, cu_ctx, C, d.outer_scale, kv_c=kv, k_pe=pe),
+        "context_attention": lambda: ops.prefill_attention(q, ctx_k, ctx_v, cu_q, Tn, *a, causal=False,
+                                                           cu_seqlens_k=cu_ctx, max_seqlen_k=C, out=part_o[:, 0],
+                                                           lse=part_l[:, 0], workspace=ws_c),
+        "new_token_attention": lambda: ops.prefill_attention(q, k, v, cu_q, Tn, *a, causal=True, out=part_o[:, 1],
+                                                             lse=part_l[:, 1], workspace=ws_n),
+        "merge": lambda: ops.lse_merge(part_o, part_l, out=out, lse=lse),
+        "quantize": lambda: ops.quantize_rows(out.view(T, H * 128), inp.g_v),
+    }
+    res = {name: timed(fn, steps, warmup) * 1e3 for name, fn in stages.items()}
+
+    def chain():
+        for fn in stages.values():
+            fn()
+
+    ms = timed(chain, steps, warmup)
+    f_ctx = 2.0 * H * Tn * C * (192 + 128) * N
+    f_new = float(N * H * 320 * Tn * (Tn + 1))
+    return {"ms": ms, "stage_us": res, "sequences": N, "context_tokens": C, "new_tokens": Tn, "heads": H,
+            "attention_tflops": (f_ctx + f_new) / (ms * 1e-3) / 1e12,
+            "context_attention_frac_mfma": f_ctx / (res["context_attention"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+            "gather_gbps": Tc * (432 + 1152) / (res["gather"] * 1e-6) / 1e9}
+
+
+def bench_decode_qdq(steps: int, warmup: int) -> dict:
+    """Decode with quantized operands on the dense decode shape (B=64, H=128,
+    L=4096, 4 splits): NVFP4 cache with Q and P NVFP4; raw bf16 cache
+    (1152-byte records, rotated over 2 copies) with Q/K/P/V NVFP4 and with
+    all four per-tensor FP8."""
+    inp = workloads.decode_workload(1)
+    dev = "cuda"
+    H, B = inp.H, inp.B
+    ntok = int(inp.seq_lens.sum())
+    q = inp.q.to(dev)
+    qn, qr = q[..., :512], q[..., 512:]
+    pt, seq = inp.page_table.to(dev), inp.seq_lens.to(dev)
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.decode_workspace_bytes(B, H, inp.max_splits), dtype=torch.uint8, device=dev)
+    kv, pe, slots = inp.kv_c.to(dev), inp.k_pe.to(dev), inp.slot_mapping.to(dev)
+
+    def scale(x, fp8):
+        return float(np.float32(float(x.abs().max()) / (448.0 if fp8 else 2688.0)))
+
+    res = {}
+    nv = torch.zeros((inp.num_pages, inp.page_size, 432), dtype=torch.uint8, device=dev)
+    ops.cache_write(kv, pe, slots, nv, inp.outer_scale)
+    nvs = [nv, nv.clone(), nv.clone(), nv.clone()]
+    raw = torch.zeros((inp.num_pages, inp.page_size, 1152), dtype=torch.uint8, device=dev)
+    ops.raw_cache_write(kv, pe, slots, raw)
+    raws = [raw, raw.clone()]
+    kvpe = torch.cat([inp.kv_c.float(), inp.k_pe.float()], 1)
+    for name, caches, flags in (("nvfp4_cache_QP", nvs, 1 | 4), ("raw_cache_QKPV", raws, 15),
+                                ("raw_cache_fp8", raws, 255)):
+        sc = dict(g_q=scale(inp.q.float(), flags & 16), g_k=scale(kvpe, flags & 32),
+                  g_v=scale(inp.kv_c.float(), flags & 128), g_p=float(np.float32(1 / (448 if flags & 64 else 2688))))
+        it = [0]
+
+        def run(caches=caches, flags=flags, sc=sc):
+            r = it[0] % len(caches)
+            it[0] += 1
+            ops.decode_qdq(qn, qr, caches[r], pt, seq, inp.outer_scale, inp.softmax_scale, flags,
+                           max_splits=inp.max_splits, out=out, lse=lse, workspace=ws, **sc)
+
+        ms = timed(run, steps, warmup)
+        rec = caches[0].shape[-1]
+        nbytes = ntok * rec + B * H * 576 * 2 + B * H * 513 * 4
+        fl = decode_flops(ntok, H)
+        res[name] = {"kernel_us": ms * 1e3, "tflops": fl / (ms * 1e-3) / 1e12,
+                     "frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "gbps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "flags": flags, "record_bytes": rec}
+    return res
 
 
 def cpu_baseline(inp, budget_s: float = 12.0):
@@ -261,8 +382,9 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         done += 1
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {inp.B} sequences (all {inp.H} heads, L={int(inp.seq_lens[0])}): oracle "
-                      f"cache write of their tokens + fp64 decode, {el:.1f} s; host cpu_count={os.cpu_count()}, "
+            "sample": f"{done} of {inp.B} sequences (all {inp.H} heads, L={int(inp.seq_lens[0])}): per query the "
+                      f"oracle writes the sequence's {int(inp.seq_lens[0])} tokens into its cache (the GPU step writes "
+                      f"one per query) then decodes in fp64, {el:.1f} s; host cpu_count={os.cpu_count()}, "
                       f"affinity={len(os.sched_getaffinity(0))}"}
 
 
@@ -308,7 +430,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16/bf16 MFMA on exact NVFP4 operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "dense NVFP4 MLA decode step: B=64, H=128, L=4096, page 64, 432-byte records, "
                                "4 splits + merge kernel, plus NVFP4 cache write of 64 new tokens",
@@ -381,9 +503,23 @@ def main():
         torch.cuda.empty_cache()
         log("cache write of the decode workload's 262,144 tokens")
         paths["cache_write"] = bench_cache_write(inp, max(10, args.steps // 2), 3)
+        paths["cache_write"]["note"] = ("its 113 MB cache fits the 256 MB Infinity Cache, which absorbs the writes; "
+                                        "cache_write_ragged is the HBM figure")
         torch.cuda.empty_cache()
         log("prefill (8 sequences of 2k-8k tokens, 128 heads, NVFP4 output)")
         paths["prefill"] = bench_prefill(max(3, args.steps // 10), 1)
+        torch.cuda.empty_cache()
+        log("prefill with per-tensor FP8 Q/K/P/V")
+        paths["prefill_fp8"] = bench_prefill(max(3, args.steps // 10), 1, flags=255)
+        torch.cuda.empty_cache()
+        log("prefill with NVFP4 Q/K/P/V and 2:4 score sparsity")
+        paths["prefill_2_4"] = bench_prefill(max(3, args.steps // 10), 1, flags=15 | 256)
+        torch.cuda.empty_cache()
+        log("chunked prefill over the NVFP4 cache (8 x 4096 context + 8 x 512 new tokens)")
+        paths["chunked_prefill"] = bench_chunked_prefill(max(3, args.steps // 5), 2)
+        torch.cuda.empty_cache()
+        log("decode with quantized operands (NVFP4 cache Q/P; raw cache Q/K/P/V NVFP4 and FP8)")
+        paths["decode_qdq"] = bench_decode_qdq(max(10, args.steps // 2), 3)
         torch.cuda.empty_cache()
         result["paths"] = paths
 
