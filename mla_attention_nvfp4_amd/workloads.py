@@ -15,7 +15,7 @@ Workloads (sizes as stated for each; the pages publish no benchmark suite):
 2  ragged decode with fp8 RoPE: B=128, H=128, L ~ U{1024..32768}, pages of
    64 shuffled, e4m3 RoPE (368-byte records), latent N(0,1) with each element
    multiplied by 20 with probability 0.01, outer scale ~ U[0.5, 2], split
-   count chosen per sequence (up to 32 splits).
+   count chosen per sequence (up to 8 splits).
 3  sparse top-k decode: B=32, H=128, L=65536 per sequence, pages of 64
    shuffled, 432-byte records, outer scale ~ U[0.5, 2]; indices [32, 2048]
    drawn without replacement from [0, 65536) with 205 entries per row
