@@ -89,7 +89,12 @@ struct DecodeSmem {
 
 
 
-template <int NW, bool kRopeFp8, bool kSparse>
+// kPQ: 0 plain decode; 1 P quantized as NVFP4 (16-key blocks), 2 as
+// per-tensor FP8 (the quantized-operand decode on NVFP4 records: the running
+// max is then exact, refreshed per tile, and P is quantized against it; the
+// quantized values are exact in the fp16 B operand, so one PV sweep).  Q may
+// be quantized at set-up (p.qdq_flags bit 1), its exact values kept.
+template <int NW, bool kRopeFp8, bool kSparse, int kPQ>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void decode_kernel(DecodeArgs p) {
     constexpr int kRec = kRopeFp8 ? 368 : 432;
@@ -141,7 +146,67 @@ void decode_kernel(DecodeArgs p) {
     // for kk < kQLdsLatent, kQLdsLatent + kk - 16 for RoPE).
     f16x8 qf[16 - kQLdsLatent];
     float q_unscale;   // 2^(E - 14)
+    float q_mul = 1.0f;   // Q quantized: its tensor-wide multiplier (applied to the whole score)
+    auto setup_q_quantized = [&]() {
+        // blocks of 16 features: block 2kk + gq/2 of k-step kk is this lane's 8
+        // values and those of lane ^ 16; the exact values s*v (or e4m3 values)
+        // are kept, fp16 for the latent (no scaling needed), bf16 for RoPE
+        const bool fp8 = p.qdq_flags & 16u;
+        const float inv_g = 1.0f / p.g_q;
+        auto qdq8 = [&](u32x4 r, float* x) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[2 * j] = bf16_lo(r[j]);
+                x[2 * j + 1] = bf16_hi(r[j]);
+            }
+            if (fp8) {
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(e4m3_encode2_hw(x[i] * inv_g, x[i + 1] * inv_g), false);
+                    x[i] = d[0];
+                    x[i + 1] = d[1];
+                }
+            } else {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(x[i]));
+                a = xor16_max(a);
+                const Nvfp4Scale sc = nvfp4_block_scale(a, p.g_q);
+                const float sv = e4m3_decode(sc.code);
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const f32x2 d = e2m1_pair<0>(e2m1_pack2<0>(0u, x[i] * sc.inv, x[i + 1] * sc.inv));
+                    x[i] = d[0] * sv;
+                    x[i + 1] = d[1] * sv;
+                }
+            }
+        };
+        q_unscale = 1.0f;
+        q_mul = p.g_q;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float x[8];
+            qdq8(qraw[kk], x);
+            f16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (_Float16)x[i];
+            if (kk < kQLdsLatent) sm.qs[w][kk][lane] = __builtin_bit_cast(u32x4, v);
+            else qf[kk - kQLdsLatent] = v;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float x[8];
+            qdq8(qrope[kk], x);
+            sm.qs[w][kQLdsLatent + kk][lane] =
+                u32x4{pack_bf16_exact(x[0], x[1]), pack_bf16_exact(x[2], x[3]), pack_bf16_exact(x[4], x[5]),
+                      pack_bf16_exact(x[6], x[7])};
+        }
+    };
     auto setup_q = [&]() {
+        if (kPQ != 0 && (p.qdq_flags & 1u)) {
+            setup_q_quantized();
+            return;
+        }
         float amax = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk)
@@ -170,8 +235,10 @@ void decode_kernel(DecodeArgs p) {
 
     const uint8_t* __restrict__ cache = p.cache;
     const float outer = p.outer_scale;
+    // P quantized: u = fp32(6 g_p), 1/u, 1/g_p
+    const float p_u = 6.0f * p.g_p, p_inv_u = kPQ != 0 ? 1.0f / p_u : 0.0f, p_inv_g = kPQ != 0 ? 1.0f / p.g_p : 0.0f;
     float lat_scale = 0.0f;                               // latent partial sum -> outer * q.k (set with Q)
-    const float score_scale = p.softmax_scale * kLog2e;   // log2 units
+    float score_scale = p.softmax_scale * kLog2e;         // log2 units (times Q's multiplier, set with Q)
     const float wide_scale = kSinglePBound / (6.0f * outer);   // block scales above this need the residual pass
 
     // ---- offsets.  Loads are issued by every lane of wavefront 0 from
@@ -360,8 +427,9 @@ void decode_kernel(DecodeArgs p) {
         mx = xor32_max(xor16_max(mx));
         // Lazy rescaling: the reference max moves only when a score exceeds
         // it by more than kRescaleSlack (log2 units), so p <= 2^8 and O is
-        // rescaled rarely.  Same softmax; only the rounding differs.
-        const bool move = mx > m_run + kRescaleSlack;
+        // rescaled rarely.  Same softmax; only the rounding differs.  With P
+        // quantized the max is exact (P is quantized against it).
+        const bool move = kPQ != 0 ? mx > m_run : mx > m_run + kRescaleSlack;
         const float m_new = move ? mx : m_run;
         const bool live = m_new != -INFINITY;
         const float alpha = (move && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -385,10 +453,43 @@ void decode_kernel(DecodeArgs p) {
         // token 16 + 4gq + j - 4 (the same slots as the V^T fragment below);
         // the residual p - fp16(p) is formed only for a tile that needs it.
         f16x8 ph;
+        if constexpr (kPQ == 0) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ph[4 * tt + i] = (_Float16)pv[tt][i];
+                for (int i = 0; i < 4; ++i) ph[4 * tt + i] = (_Float16)pv[tt][i];
+        } else {
+            // P block tt (16 keys) of head c16: this lane's 4 values and those
+            // of lanes c16 + 16g'; the quantized values are exact in fp16
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                if constexpr (kPQ == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t c2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                            fminf(pv[tt][i] * p_inv_g, 448.0f), fminf(pv[tt][i + 1] * p_inv_g, 448.0f), 0, false);
+                        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+                        ph[4 * tt + i] = (_Float16)d[0];
+                        ph[4 * tt + i + 1] = (_Float16)d[1];
+                    }
+                } else {
+                    float a = fmaxf(fmaxf(pv[tt][0], pv[tt][1]), fmaxf(pv[tt][2], pv[tt][3]));
+                    a = xor32_max(xor16_max(a));
+                    float tq = a * p_inv_u;
+                    if (scale_quotient_near_tie(tq)) tq = a / p_u;
+                    const uint32_t code = e4m3_encode_nonneg(tq);
+                    const float sv = e4m3_decode(code);
+                    const float dd = sv * p.g_p;
+                    const float inv = dd == 0.0f ? 0.0f : 1.0f / dd;
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const f32x2 d = e2m1_pair<0>(e2m1_pack2<0>(0u, pv[tt][i] * inv, pv[tt][i + 1] * inv));
+                        ph[4 * tt + i] = (_Float16)(d[0] * sv);
+                        ph[4 * tt + i + 1] = (_Float16)(d[1] * sv);
+                    }
+                }
+            }
+        }
         // V^T fragment of column tile c by transposing reads: within each
         // 16-lane group, lane s addresses token 4gq + s/4 (+16 for the
         // second half) and columns 16c + 4(s%4) .. +3; lane i receives the 4
@@ -432,7 +533,7 @@ void decode_kernel(DecodeArgs p) {
         // (the flags are the same in every lane: a uniform branch)
         const bool wide = __builtin_amdgcn_readfirstlane(wo[0] | wo[1] | wo[2] | wo[3]) != 0u;
         wide_seen = wide_seen || wide;
-        if (wide) {
+        if (kPQ == 0 && wide) {
             f16x8 pl;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -454,6 +555,7 @@ void decode_kernel(DecodeArgs p) {
             }
             setup_q();
             lat_scale = outer * q_unscale;
+            score_scale *= q_mul;
             if (w == 0) {
 #pragma unroll
                 for (int k = 0; k < 3; ++k) store_offs(k, offset_of(pos0[k], pg0[k]));
@@ -490,7 +592,7 @@ void decode_kernel(DecodeArgs p) {
     }
 
     const bool any = l_run > 0.0f;
-    const float so = any ? outer / l_run : 0.0f;
+    const float so = any ? (kPQ != 0 ? outer * p.g_p : outer) / l_run : 0.0f;
     const float lse_v = any ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
     const bool has_head = wave_active && hq < p.H;
     if (ns == 1) {
@@ -709,11 +811,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     if (a.lse && lane == 0) a.lse[(int64_t)b * a.H + h] = M + logf(wsum);
 }
 
-template <int NW, bool kRopeFp8, bool kSparse>
+template <int NW, bool kRopeFp8, bool kSparse, int kPQ = 0>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int hg = 16 * NW;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.B, (unsigned)((a.H + hg - 1) / hg));
-    hipLaunchKernelGGL((decode_kernel<NW, kRopeFp8, kSparse>), grid, dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<NW, kRopeFp8, kSparse, kPQ>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -730,6 +832,17 @@ hipError_t launch_decode_w(const DecodeArgs& a, hipStream_t stream) {
 // Up to 16 heads: the narrow kernel (each wavefront its own tokens); more:
 // 128 heads per workgroup.  Split sequences are then merged by
 // split_merge_kernel.
+// Dense decode on NVFP4 records with P quantized (and Q, by p.qdq_flags), for
+// more than 16 heads; the split merge follows.
+hipError_t launch_decode_pq(const DecodeArgs& a, hipStream_t stream) {
+    const bool fp8r = a.record_bytes == 368, fp8p = a.qdq_flags & 64u;
+    hipError_t e;
+    if (fp8p) e = fp8r ? launch_decode_t<8, true, false, 2>(a, stream) : launch_decode_t<8, false, false, 2>(a, stream);
+    else e = fp8r ? launch_decode_t<8, true, false, 1>(a, stream) : launch_decode_t<8, false, false, 1>(a, stream);
+    if (e != hipSuccess || a.max_splits <= 1) return e;
+    return launch_split_merge(a, stream);
+}
+
 hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream) {
     const int64_t waves = (int64_t)a.B * a.H;
     if (a.indices)

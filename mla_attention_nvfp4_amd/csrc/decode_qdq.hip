@@ -503,6 +503,16 @@ hipError_t launch_qdq_t(const QdqParams& pp, hipStream_t stream) {
 
 hipError_t launch_decode_qdq(const DecodeArgs& a, unsigned flags, float g_q, float g_k, float g_v, float g_p,
                              hipStream_t stream) {
+    // NVFP4 records, more than 16 heads, P quantized: the 128-head decode
+    // kernel with P (and Q) quantization (same schedule: each wavefront walks
+    // its split's 32-token tiles in order with one running max)
+    if (a.record_bytes != 1152 && a.H > 16 && (flags & 4u)) {
+        DecodeArgs b = a;
+        b.qdq_flags = flags;
+        b.g_q = g_q;
+        b.g_p = g_p;
+        return launch_decode_pq(b, stream);
+    }
     QdqParams pp{a, flags, g_q, g_k, g_v, g_p};
     hipError_t e;
     if (a.record_bytes == 1152) {

@@ -43,10 +43,17 @@ struct DecodeArgs {
     uint8_t* ws_fmt;          // [B][max_splits][H]: 1 = that partial row is fp16, 0 = fp32
     float* out;               // [B][H][512]
     float* lse;               // [B][H]
+    // quantized operands (decode_kernel with P quantized; 0 = plain decode):
+    // bit 1 Q quantized (bit 16: as per-tensor FP8), multipliers g_q, g_p
+    unsigned qdq_flags;
+    float g_q, g_p;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_narrow(const DecodeArgs& a, hipStream_t stream);   // H <= 16
+// Dense decode on NVFP4 records (H > 16) with P quantized (a.qdq_flags bit 4;
+// FP8 with bit 64) and Q by bit 1 / 16, a.g_q, a.g_p; then the split merge.
+hipError_t launch_decode_pq(const DecodeArgs& a, hipStream_t stream);
 // Merge of a decode launch's split partials (after the decode kernel).
 hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream);
 // Decode with quantized operands (dense; record_bytes 432, 368 or 1152 raw).
