@@ -226,10 +226,9 @@ struct AttnParams {
     const int32_t* cu;        // query rows of sequence n: [cu[n], cu[n+1])
     const int32_t* ck;        // key rows of sequence n (context attention): [ck[n], ck[n+1])
     int causal;               // keys are the query rows, row i sees keys j <= i
-    int sparse24;             // 2:4 score sparsity
-    int score_pos;            // softmax_scale > 0 (else every score ties for the 2:4 choice)
     int H;
     float score_scale_log2;   // softmax_scale * g_q' * g_k' * log2(e)
+    float rank_mul;           // 2:4 ranking factor: 1, or 0 when softmax_scale is 0 (every score ties)
     double out_scale;         // g_p' * g_v' (exact in fp64)
     float g_p;                // P multiplier (P quantized only)
     float u_p;                // fp32(6 g_p)
@@ -290,11 +289,12 @@ struct BoolTag {
 // FP4 or FP8 conversion; otherwise they run in bf16 (quantized P exact,
 // unquantized P split into three bf16 parts).
 //
-// 2:4 sparsity: in a score tile, a lane's elements 4c .. 4c+3 are 4
-// consecutive keys starting at a multiple of 4, so each group's choice is
-// made within one lane, on the raw fp32 accumulators (the scale factors are
-// common to the row and positive; softmax_scale = 0 makes every score tie).
-template <int kPMode, bool kF16>
+// 2:4 sparsity (kSparse): in a score tile, a lane's elements 4c .. 4c+3
+// are 4 consecutive keys starting at a multiple of 4, so each group's choice
+// is made within one lane, on the raw fp32 accumulators (the scale factors
+// are common to the row and positive; softmax_scale = 0 makes every score
+// tie).
+template <int kPMode, bool kF16, bool kSparse>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnParams p) {
     constexpr bool kQuantP = kPMode != 0;
@@ -468,48 +468,63 @@ void attn_kernel(AttnParams p) {
         // since fp32(c x) is monotone in x for c >= 0, and each exponent is
         // one fused c * s - m)
         float mx = -INFINITY;
+        // element v of score tile mt2 is key 32 mt2 + 8 (v / 4) + v % 4 of
+        // this lane's quarter of the tile; with 2:4 sparsity, of each group
+        // of 4 keys (elements 4c .. 4c+3) the two outranked by two others are
+        // dropped: key i beats key j > i when x_i >= x_j (equal scores rank
+        // by index), one comparison per pair
+        auto two_of = [](bool x, bool y, bool z) { return (x && y) || (z && (x || y)); };
+        auto drop_2_4 = [&](float x0, float x1, float x2, float x3, bool (&d)[4]) {
+            const bool b01 = x0 >= x1, b02 = x0 >= x2, b03 = x0 >= x3;
+            const bool b12 = x1 >= x2, b13 = x1 >= x3, b23 = x2 >= x3;
+            d[0] = two_of(!b01, !b02, !b03);
+            d[1] = two_of(b01, !b12, !b13);
+            d[2] = two_of(b02, b12, !b23);
+            d[3] = two_of(b03, b13, b23);
+        };
         if constexpr (kMask) {
-            // keys past this row's last key are masked; with 2:4 sparsity,
-            // of each group of 4 the keys outranked by two others too
-            // bit 16 mt2 + v of vis: element v of score tile mt2 is seen
+            // keys past this row's last key are masked; the 2:4 ranking sees
+            // them as -inf and ranks the raw scores (times rank_mul: 0 when
+            // softmax_scale is 0, which makes every seen score tie)
             const int rel = lim - (kt * kBN + 4 * g2);   // last key offset this lane's row sees
-            uint32_t vis = 0u;
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    vis |= (32 * mt2 + 8 * (v >> 2) + (v & 3) <= rel ? 1u : 0u) << (16 * mt2 + v);
-            if (p.sparse24) {   // (uniform)
+                for (int c = 0; c < 4; ++c) {
+                    bool seen[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) seen[i] = 32 * mt2 + 8 * c + i <= rel;
+                    if constexpr (kSparse) {
+                        float x[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[i] = seen[i] ? p.rank_mul * s[mt2][4 * c + i] : -INFINITY;
+                        bool d[4];
+                        drop_2_4(x[0], x[1], x[2], x[3], d);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) seen[i] = seen[i] && !d[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float z = seen[i] ? c_log2 * s[mt2][4 * c + i] : -INFINITY;
+                        s[mt2][4 * c + i] = z;
+                        mx = fmaxf(mx, z);
+                    }
+                }
+        } else {
+            // (with 2:4 sparsity the tile is ranked on the raw scores: the
+            // caller sends tiles here only when softmax_scale > 0)
+            if constexpr (kSparse) {
 #pragma unroll
                 for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const int b0 = 16 * mt2 + 4 * c;
-                        float x[4];
+                        bool d[4];
+                        drop_2_4(s[mt2][4 * c], s[mt2][4 * c + 1], s[mt2][4 * c + 2], s[mt2][4 * c + 3], d);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            x[i] = ((vis >> (b0 + i)) & 1u) ? (p.score_pos ? s[mt2][4 * c + i] : 0.0f) : -INFINITY;
-                        uint32_t drop = 0u;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            int rank = 0;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                if (j != i) rank += (x[j] > x[i] || (x[j] == x[i] && j < i)) ? 1 : 0;
-                            drop |= (rank >= 2 ? 1u : 0u) << (b0 + i);
-                        }
-                        vis &= ~drop;
+                            if (d[i]) s[mt2][4 * c + i] = -INFINITY;
                     }
             }
-#pragma unroll
-            for (int mt2 = 0; mt2 < 2; ++mt2)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float z = ((vis >> (16 * mt2 + v)) & 1u) ? c_log2 * s[mt2][v] : -INFINITY;
-                    s[mt2][v] = z;
-                    mx = fmaxf(mx, z);
-                }
-        } else {
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
@@ -705,7 +720,7 @@ void attn_kernel(AttnParams p) {
         // (unless the 2:4 choice masks keys)
         if (wave_rows && (!p.causal || kt * kBN <= wave_last_row)) {
             const bool full = p.causal ? kt * kBN + kBN - 1 <= wr0 : kt * kBN + kBN <= Lk;
-            if (full && !p.sparse24) compute(kt, kt & 1, vbuf, BoolTag<false>{}, defer);
+            if (full && (!kSparse || p.rank_mul != 0.0f)) compute(kt, kt & 1, vbuf, BoolTag<false>{}, defer);
             else compute(kt, kt & 1, vbuf, BoolTag<true>{}, defer);
             if constexpr (kQuantP && kF16) {
                 if (defer) held = vbuf;
@@ -789,6 +804,12 @@ __global__ __launch_bounds__(256) void pad_scales_kernel(uint8_t* scales, int64_
     scales[swizzled_scale_offset(m, c, cpad)] = 0;
 }
 
+template <int kPMode, bool kF16>
+void launch_attn(bool sparse, dim3 grid, dim3 block, hipStream_t stream, const AttnParams& p) {
+    if (sparse) hipLaunchKernelGGL((attn_kernel<kPMode, kF16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_kernel<kPMode, kF16, false>), grid, block, 0, stream, p);
+}
+
 }  // namespace
 
 int prefill_p_tile() { return kBN; }
@@ -863,10 +884,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.cu = a.cu_seqlens;
     p.ck = cuk;
     p.causal = causal ? 1 : 0;
-    p.sparse24 = (f & 256u) ? 1 : 0;
-    p.score_pos = a.softmax_scale > 0.0f ? 1 : 0;
     p.H = H;
     p.score_scale_log2 = a.softmax_scale * gq * gk * kLog2e;
+    p.rank_mul = a.softmax_scale > 0.0f ? 1.0f : 0.0f;
     p.out_scale = (double)gp * (double)gv;
     p.g_p = a.g_p;
     p.u_p = 6.0f * a.g_p;
@@ -886,14 +906,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         const dim3 grid((unsigned)((a.max_seqlen + kBM - 1) / kBM), (unsigned)H, (unsigned)a.N);
         const dim3 block(kWaves * 64);
         const bool fp8p = f & 64u;
+        const bool sp = f & 256u;
         if (qP && qV) {
-            if (fp8p) hipLaunchKernelGGL((attn_kernel<2, true>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((attn_kernel<1, true>), grid, block, 0, stream, p);
+            if (fp8p) launch_attn<2, true>(sp, grid, block, stream, p);
+            else launch_attn<1, true>(sp, grid, block, stream, p);
         } else if (qP) {
-            if (fp8p) hipLaunchKernelGGL((attn_kernel<2, false>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((attn_kernel<1, false>), grid, block, 0, stream, p);
+            if (fp8p) launch_attn<2, false>(sp, grid, block, stream, p);
+            else launch_attn<1, false>(sp, grid, block, stream, p);
         } else {
-            hipLaunchKernelGGL((attn_kernel<0, false>), grid, block, 0, stream, p);
+            launch_attn<0, false>(sp, grid, block, stream, p);
         }
     }
     if (a.out_fp4) {

@@ -19,7 +19,7 @@ from oracle import formats as F
 from oracle import prefill as P
 from oracle import record as R
 from oracle import swizzle as S
-from test_gpu_prefill import _compare, _run_gpu, p_tie_rows
+from test_gpu_prefill import _compare, _run_gpu, p_tie_rows, sparse_tie_keeps
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,16 @@ GRID = [
     (32, [90, 33], 2, 256 | 12),                    # with P and V NVFP4 (fp16 PV products)
     (33, [64, 129], 2, 256 | 4 | 64 | 8),           # with P FP8, V NVFP4
 ]
+
+
+@pytest.mark.parametrize("flags", [256, 15 | 256])
+def test_prefill_sparsity_zero_scale(flags):
+    """softmax_scale 0: every seen score is 0, so each group of 4 keeps its
+    first two seen keys and P is 1 on them (the ranking must not use the raw
+    products)."""
+    inp = workloads.prefill_inputs(461, [1, 3, 6, 70, 133], 2, flags)
+    inp.softmax_scale = 0.0
+    _compare(inp, _run_gpu(inp), [0, 1], None, f"zero-scale flags {flags}")
 
 
 @pytest.mark.parametrize("case", GRID, ids=[f"grid{c[0]}-flags{c[3]}" for c in GRID])
@@ -118,16 +128,16 @@ CTX = [
     (42, [64, 17], [512, 300], 2, 11),            # Q, K, V NVFP4 (no P: schedule-free)
     (43, [33, 1, 90], [257, 64, 1000], 2, 15),    # all four NVFP4
     (44, [20, 70], [130, 600], 3, 255),           # all four FP8
+    (45, [30, 9, 64], [200, 67, 0], 2, 15 | 256),  # all four NVFP4, 2:4 sparsity
+    (46, [12, 5], [130, 3], 2, 255 | 256),        # all four FP8, 2:4 sparsity
 ]
 
 
-@pytest.mark.parametrize("case", CTX, ids=[f"ctx{c[0]}-flags{c[4]}" for c in CTX])
-def test_context_attention(case):
-    """New tokens over their sequences' cached context (every key visible),
-    fp32 output and LSE."""
-    seed, new_lens, ctx_lens, H, flags = case
+def _context_case(seed, new_lens, ctx_lens, H, flags, softmax_scale=None):
     ci = workloads.context_inputs(400 + seed, new_lens, ctx_lens, H, flags)
     inp = ci.new
+    if softmax_scale is not None:
+        inp.softmax_scale = softmax_scale
     out, lse = _gpu_attention(inp.q.cuda(), ci.ctx_k.cuda(), ci.ctx_v.cuda(), inp.cu_seqlens.cuda(), inp.max_seqlen,
                               inp, flags, False, ci.cu_ctx.cuda(), ci.max_ctx)
     torch.cuda.synchronize()
@@ -140,14 +150,35 @@ def test_context_attention(case):
     mult = P.operand_multipliers(flags, inp.g_q, inp.g_k)
 
     def alt_rows(t, h):
-        if not flags & P.FLAG_P:
-            return []
+        # the oracle's rows under P rounding decisions near a boundary, or
+        # under exchanges of near-equal scores in the 2:4 choice
         n = int(np.searchsorted(cq, t, side="right") - 1)
         a, ka, kb = int(cq[n]), int(cc[n]), int(cc[n + 1])
-        return p_tie_rows(qh[a:int(cq[n + 1]), h], kh[ka:kb, h], vh[ka:kb, h], t - a, inp.softmax_scale, flags,
-                          inp.g_p, False, mult) or []
+        qs, ks, vs = qh[a:int(cq[n + 1]), h], kh[ka:kb, h], vh[ka:kb, h]
+        alts = []
+        if flags & P.FLAG_P:
+            alts += p_tie_rows(qs, ks, vs, t - a, inp.softmax_scale, flags, inp.g_p, False, mult) or []
+        if flags & P.SPARSE_2_4 and inp.softmax_scale != 0:
+            for fn in (sparse_tie_keeps(qs, ks, t - a, False, mult) or [])[1:]:
+                alts.append(P.attend_rows(qs, ks, vs, [t - a], inp.softmax_scale, bool(flags & P.FLAG_P), inp.g_p,
+                                          causal=False, sparse_2_4=True, p_fp8=bool(flags & P.FP8_P),
+                                          multipliers=mult, keep_fn=fn))
+        return alts
 
     _check_rows(out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_l, alt_rows, f"ctx{seed}")
+
+
+@pytest.mark.parametrize("case", CTX, ids=[f"ctx{c[0]}-flags{c[4]}" for c in CTX])
+def test_context_attention(case):
+    """New tokens over their sequences' cached context (every key visible),
+    fp32 output and LSE."""
+    _context_case(*case)
+
+
+def test_context_attention_sparsity_zero_scale():
+    """2:4 over the cached context with softmax_scale 0: the first two keys
+    of every group of 4, P = 1 on them."""
+    _context_case(47, [7, 20], [70, 129], 2, 15 | 256, softmax_scale=0.0)
 
 
 def test_causal_attention_fp32_output_matches_fused_path():
