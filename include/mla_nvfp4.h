@@ -436,6 +436,31 @@ int mla_nvfp4_cache_gather(const uint8_t* cache, int64_t num_pages, int record_b
 int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale,
                             uint8_t* codes, uint8_t* scales_swizzled, void* stream);
 
+/* Roofline re-measurement helpers (not part of the attention path): an MFMA
+ * micro-benchmark and two stream kernels, so that the vendor peaks the
+ * roofline fractions are quoted against can be checked on the part.  The
+ * caller times the launches (HIP events on `stream`) and derives the rates.
+ *
+ * mla_roofline_mfma: `blocks` workgroups of 4 wavefronts, each running
+ * `iters` iterations of 8 independent fp16 products with operands in
+ * registers: shape 0 = v_mfma_f32_16x16x32_f16 (16,384 flops each), shape 1 =
+ * v_mfma_f32_32x32x16_f16 (32,768 flops each).  One float per lane is
+ * written to `sink` (float [blocks * 256]) so that nothing is removed.
+ *
+ * mla_roofline_copy: a plain copy of `bytes` (a multiple of 16, 16-byte
+ * aligned buffers, not overlapping) from src to dst, 16 bytes per lane.
+ *
+ * mla_roofline_read: reads `bytes` (a multiple of 16) of src (16-byte
+ * aligned) and adds the wrapping 32-bit sum of its little-endian 32-bit words
+ * to *sum (device uint32, 4-byte aligned; the caller zeroes it).  bytes == 0
+ * launches nothing.
+ *
+ * All three return MLA_ERR_INVALID_ARGUMENT for arguments outside these
+ * ranges, before any launch. */
+int mla_roofline_mfma(int shape, int blocks, int iters, float* sink, void* stream);
+int mla_roofline_copy(const void* src, void* dst, int64_t bytes, void* stream);
+int mla_roofline_read(const void* src, int64_t bytes, uint32_t* sum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,9 @@ SIGNATURES = {
     "mla_nvfp4_cache_gather": (c_int, [c_p, c_i64, c_int, c_int, c_p, c_int, c_p, c_p, c_int, c_int, c_i64, c_f32,
                                        c_p, c_i64, c_p, c_i64, c_p]),
     "mla_nvfp4_quantize_rows": (c_int, [c_p, c_i64, c_int, c_f32, c_p, c_p, c_p]),
+    "mla_roofline_mfma": (c_int, [c_int, c_int, c_int, c_p, c_p]),
+    "mla_roofline_copy": (c_int, [c_p, c_p, c_i64, c_p]),
+    "mla_roofline_read": (c_int, [c_p, c_i64, c_p, c_p]),
 }
 
 MLA_QDQ_Q, MLA_QDQ_K, MLA_QDQ_P, MLA_QDQ_V = 1, 2, 4, 8
@@ -397,3 +400,36 @@ def quantize_rows(x, global_scale):
     _check(lib().mla_nvfp4_quantize_rows(x.data_ptr(), M, K, float(global_scale), codes.data_ptr(),
                                          scales.data_ptr(), _stream(x)))
     return codes, scales
+
+
+# ---------------------------------------------------------------- roofline --
+
+def roofline_mfma(shape: int, blocks: int, iters: int, sink: torch.Tensor) -> None:
+    """Launch the MFMA-rate kernel (shape 0: 16x16x32 f16, 1: 32x32x16 f16;
+    8 products per wavefront and iteration, 4 wavefronts per workgroup) on
+    the current stream; ``sink`` is float32 [blocks * 256] on the device."""
+    _need(sink, torch.float32, "sink")
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink needs blocks * 256 floats")
+    _check(lib().mla_roofline_mfma(shape, blocks, iters, _ptr(sink), _stream(sink)))
+
+
+def roofline_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Plain device copy of src's bytes into dst (same byte size, 16-byte
+    aligned, multiple of 16 bytes) on the current stream."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous with the same byte size")
+    _check(lib().mla_roofline_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
+
+
+def roofline_read(src: torch.Tensor, total: torch.Tensor) -> None:
+    """Read-only stream over src's bytes (contiguous, 16-byte aligned,
+    multiple of 16 bytes) on the current stream: adds the wrapping 32-bit
+    sum of its words to ``total`` (int32 [1] on the device, not zeroed)."""
+    _need(total, torch.int32, "total")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().mla_roofline_read(_ptr(src), nbytes, _ptr(total), _stream(src)))
+

@@ -12,6 +12,7 @@
 
 #include "../../include/mla_nvfp4.h"
 #include "launch.hpp"
+#include "roofline.hpp"
 
 namespace {
 
@@ -607,6 +608,36 @@ int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale
     return hip_status(mla::launch_quantize_rows(x, M, K, global_scale, codes, scales_swizzled,
                                                 static_cast<hipStream_t>(stream)),
                       "quantize_rows launch");
+}
+
+int mla_roofline_mfma(int shape, int blocks, int iters, float* sink, void* stream) {
+    if (shape != 0 && shape != 1) return fail(MLA_ERR_INVALID_ARGUMENT, "shape must be 0 (16x16x32) or 1 (32x32x16)");
+    if (blocks < 1 || blocks > 65536 || iters < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "need 1 <= blocks <= 65536, iters >= 0");
+    if (!sink) return fail(MLA_ERR_INVALID_ARGUMENT, "null sink");
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_mfma_rate(shape, blocks, iters, sink, static_cast<hipStream_t>(stream)), "mfma rate launch");
+}
+
+int mla_roofline_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must be a non-negative multiple of 16");
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(MLA_ERR_INVALID_ARGUMENT, "src and dst must be 16-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "stream copy launch");
+}
+
+int mla_roofline_read(const void* src, int64_t bytes, uint32_t* sum, void* stream) {
+    if (bytes < 0 || bytes % 16) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must be a non-negative multiple of 16");
+    if (!sum) return fail(MLA_ERR_INVALID_ARGUMENT, "null sum");
+    if (bytes == 0) return ok();
+    if (!src) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned(src, 16) || !aligned(sum, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "src must be 16-byte and sum 4-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    return hip_status(mla::launch_stream_read(src, bytes, sum, static_cast<hipStream_t>(stream)), "stream read launch");
 }
 
 }  // extern "C"
