@@ -369,20 +369,43 @@ void attn_kernel(AttnParams p) {
     const int nkt = p.causal ? (rows_end + kBN - 1) / kBN : (Lk + kBN - 1) / kBN;
     const int wave_last_row = min(wr0 + kRowsPerWave, L) - 1;
 
-    // K/V tile staging: K 64 rows x 24 chunks (3 per thread), V 64 x 16 (2 per thread)
+    // K/V tile staging: K 64 rows x 24 chunks (3 per thread), V 64 x 16 (2
+    // per thread).  Each thread's chunk pointers are formed once, at its row
+    // of tile 0; a whole tile adds a uniform stride, and the last, partial
+    // tile clamps rows to key Lk - 1.
     u32x4 sk[3], sv[2];
+    const uint16_t* kp[3];
+    const uint16_t* vp[2];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int c = tid + 512 * i;
+        kp[i] = p.k + (int64_t)(ka + c / 24) * p.k_st + (int64_t)h * p.k_sh + 8 * (c % 24);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 512 * i;
+        vp[i] = p.v + (int64_t)(ka + (c >> 4)) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15);
+    }
     auto load_tile = [&](int kt) {
+        if (kt * kBN + kBN <= Lk) {
+            const int64_t ko = (int64_t)(kt * kBN) * p.k_st, vo = (int64_t)(kt * kBN) * p.v_st;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int c = tid + 512 * i;
-            const int j = min(kt * kBN + c / 24, Lk - 1);
-            sk[i] = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(ka + j) * p.k_st + (int64_t)h * p.k_sh + 8 * (c % 24));
-        }
+            for (int i = 0; i < 3; ++i) sk[i] = *reinterpret_cast<const u32x4*>(kp[i] + ko);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i;
-            const int j = min(kt * kBN + (c >> 4), Lk - 1);
-            sv[i] = *reinterpret_cast<const u32x4*>(p.v + (int64_t)(ka + j) * p.v_st + (int64_t)h * p.v_sh + 8 * (c & 15));
+            for (int i = 0; i < 2; ++i) sv[i] = *reinterpret_cast<const u32x4*>(vp[i] + vo);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int r = (tid + 512 * i) / 24;
+                const int j = min(kt * kBN + r, Lk - 1);
+                sk[i] = *reinterpret_cast<const u32x4*>(kp[i] + (int64_t)(j - r) * p.k_st);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = (tid + 512 * i) >> 4;
+                const int j = min(kt * kBN + r, Lk - 1);
+                sv[i] = *reinterpret_cast<const u32x4*>(vp[i] + (int64_t)(j - r) * p.v_st);
+            }
         }
     };
     auto store_tile = [&](int buf, int vbuf) {
