@@ -53,8 +53,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 struct QdqSmem {
     uint16_t kt[kTile * kPitch];   // K tile: latent (fp16 or bf16) then RoPE (bf16)
     uint16_t vt[kTile * kPitch];   // V tile: latent (fp16 or bf16)
-    int64_t offs[kTile];           // record byte offsets (masked tokens: 0)
-    uint32_t valid;                // bit i: token i of the tile is unmasked
+    int64_t offs[2][kTile];        // record byte offsets of tiles t, t+1 (masked tokens: 0)
+    uint32_t valid[2];             // bit i: token i of the tile is unmasked
 };
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
@@ -223,24 +223,37 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     const uint8_t* __restrict__ cache = p.cache;
-    for (int t = 0; t < ntiles; ++t) {
-        const int base = i0 + kTile * t;
-        // ---- offsets of the tile's tokens
-        if (tid < kTile) {
-            const int pos = base + tid;
-            int64_t off = -1;
-            if (pos < i1) {
-                int pi, rem;
-                page_divmod(pos, p.page_size, p.page_recip, pi, rem);
-                const int pg = p.page_table[(int64_t)b * p.max_pages + pi];
-                if (pg >= 0 && pg < p.num_pages) off = ((int64_t)pg * p.page_size + rem) * kRec;
-            }
-            const uint64_t vm = __ballot(off >= 0);
-            sm.offs[tid] = off < 0 ? 0 : off;
-            if (tid == 0) sm.valid = (uint32_t)vm;
+    // Page walk of tile t into offset slot t % 2 by threads 0..31: the page-
+    // table entry is requested at the start of the previous tile and the
+    // offset stored at its end, so that the load overlaps that tile's work.
+    int pg_next = -1;
+    auto walk_request = [&](int t) {
+        const int pos = i0 + kTile * t + tid;
+        int pi, rem;
+        page_divmod(min(pos, max(i1 - 1, 0)), p.page_size, p.page_recip, pi, rem);
+        pg_next = p.page_table[(int64_t)b * p.max_pages + pi];
+    };
+    auto walk_store = [&](int t) {
+        const int pos = i0 + kTile * t + tid;
+        int64_t off = -1;
+        if (t < ntiles && pos < i1 && pg_next >= 0 && pg_next < p.num_pages) {
+            int pi, rem;
+            page_divmod(pos, p.page_size, p.page_recip, pi, rem);
+            off = ((int64_t)pg_next * p.page_size + rem) * kRec;
         }
-        __syncthreads();
-        const uint32_t vmask = sm.valid;
+        const uint64_t vm = __ballot(off >= 0);
+        sm.offs[t & 1][tid] = off < 0 ? 0 : off;
+        if (tid == 0) sm.valid[t & 1] = (uint32_t)vm;
+    };
+    if (tid < kTile && ntiles > 0) {
+        walk_request(0);
+        walk_store(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (tid < kTile) walk_request(t + 1);
+        const int64_t* offs = sm.offs[t & 1];
+        const uint32_t vmask = sm.valid[t & 1];
         // ---- staging
         if constexpr (!kRaw) {
             // 32 tokens x 64 chunks of 8 latent elements: code word + block scale
@@ -248,7 +261,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             for (int k = 0; k < 8; ++k) {
                 const int c = tid + 256 * k;
                 const int tok = c >> 6, ch = c & 63;
-                const uint8_t* rp = cache + sm.offs[tok];
+                const uint8_t* rp = cache + offs[tok];
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(rp + 4 * ch);
                 const float scf = ((vmask >> tok) & 1u) ? e4m3_decode(rp[256 + (ch >> 1)]) : 0.0f;
                 const _Float16 sh = (_Float16)scf;
@@ -264,7 +277,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             }
             {   // RoPE: 32 tokens x 8 units of 8 values
                 const int tok = tid >> 3, un = tid & 7;
-                const uint8_t* rp = cache + sm.offs[tok];
+                const uint8_t* rp = cache + offs[tok];
                 u32x4 wv;
                 if (kCache == 1) {
                     const u32x2 r2 = *reinterpret_cast<const u32x2*>(rp + 288 + 8 * un);
@@ -277,20 +290,39 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 *reinterpret_cast<u32x4*>(&sm.kt[tok * kPitch + kLatent + 8 * un]) = ((vmask >> tok) & 1u) ? wv : zero;
             }
         } else {
-            // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE)
+            // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE),
+            // V: 2 blocks of 16 tokens (absolute positions base, base + 16) x
+            // 128 groups of 4 dims.  Every load of the tile is issued before
+            // any of them is used (K indices clamped, so every address is a
+            // record of the tile).
+            constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + 255) / 256;
+            u32x4 kw[kKIt][2];
+#pragma unroll
+            for (int j = 0; j < kKIt; ++j) {
+                const int i = min(tid + 256 * j, kKBlk - 1);
+                const u32x4* src = reinterpret_cast<const u32x4*>(cache + offs[i / 36] + 32 * (i % 36));
+                kw[j][0] = src[0];
+                kw[j][1] = src[1];
+            }
+            const int half = tid >> 7, d0 = 4 * (tid & 127);
+            u32x2 vr[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const u32x2*>(cache + offs[16 * half + i] + 2 * d0);
             const float inv_gk = 1.0f / pp.g_k;
-            for (int i = tid; i < kTile * 36; i += 256) {
+#pragma unroll
+            for (int j = 0; j < kKIt; ++j) {
+                const int i = tid + 256 * j;
+                if (i >= kKBlk) break;
                 const int tok = i / 36, blk = i % 36;
                 const bool ok = (vmask >> tok) & 1u;
-                const u32x4* src = reinterpret_cast<const u32x4*>(cache + sm.offs[tok] + 32 * blk);
-                const u32x4 w0 = src[0], w1 = src[1];
+                const u32x4 w0 = kw[j][0], w1 = kw[j][1];
                 float x[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[2 * j] = ok ? bf16_lo(w0[j]) : 0.0f;
-                    x[2 * j + 1] = ok ? bf16_hi(w0[j]) : 0.0f;
-                    x[8 + 2 * j] = ok ? bf16_lo(w1[j]) : 0.0f;
-                    x[8 + 2 * j + 1] = ok ? bf16_hi(w1[j]) : 0.0f;
+                for (int jj = 0; jj < 4; ++jj) {
+                    x[2 * jj] = ok ? bf16_lo(w0[jj]) : 0.0f;
+                    x[2 * jj + 1] = ok ? bf16_hi(w0[jj]) : 0.0f;
+                    x[8 + 2 * jj] = ok ? bf16_lo(w1[jj]) : 0.0f;
+                    x[8 + 2 * jj + 1] = ok ? bf16_hi(w1[jj]) : 0.0f;
                 }
                 if (qK) qdq16(x, fK, pp.g_k, inv_gk);
                 u32x4 a, c;
@@ -305,18 +337,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 dst[0] = a;
                 dst[1] = c;
             }
-            // V: 2 blocks of 16 tokens (absolute positions base, base + 16) x
-            // 128 groups of 4 dims; per dim the block's amax (NVFP4) or each
-            // element (FP8)
+            // V: per dim the block's amax (NVFP4) or each element (FP8)
             {
-                const int half = tid >> 7, d0 = 4 * (tid & 127);
                 const float inv_gv = 1.0f / pp.g_v;
                 float x[4][16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tok = 16 * half + i;
                     const bool ok = (vmask >> tok) & 1u;
-                    const u32x2 r = *reinterpret_cast<const u32x2*>(cache + sm.offs[tok] + 2 * d0);
+                    const u32x2 r = vr[i];
                     x[0][i] = ok ? bf16_lo(r[0]) : 0.0f;
                     x[1][i] = ok ? bf16_hi(r[0]) : 0.0f;
                     x[2][i] = ok ? bf16_lo(r[1]) : 0.0f;
@@ -468,6 +497,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 for (int c = 0; c < 32; ++c) o[c] = mfma16x16x32(as_bf16x8(vt_frag(c)), bp, o[c]);
             }
         }
+        if (tid < kTile) walk_store(t + 1);
         __syncthreads();   // the tiles are restaged next iteration
     }
 
