@@ -292,9 +292,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
         } else {
             // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE),
             // V: 2 blocks of 16 tokens (absolute positions base, base + 16) x
-            // 128 groups of 4 dims.  Every load of the tile is issued before
-            // any of them is used (K indices clamped, so every address is a
-            // record of the tile).
+            // 128 groups of 4 dims.  All K loads are issued before any is
+            // used (indices clamped, so every address is a record of the
+            // tile), then all V loads.
             constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + 255) / 256;
             u32x4 kw[kKIt][2];
 #pragma unroll
@@ -305,9 +305,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 kw[j][1] = src[1];
             }
             const int half = tid >> 7, d0 = 4 * (tid & 127);
-            u32x2 vr[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const u32x2*>(cache + offs[16 * half + i] + 2 * d0);
             const float inv_gk = 1.0f / pp.g_k;
 #pragma unroll
             for (int j = 0; j < kKIt; ++j) {
@@ -338,6 +335,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 dst[1] = c;
             }
             // V: per dim the block's amax (NVFP4) or each element (FP8)
+            u32x2 vr[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const u32x2*>(cache + offs[16 * half + i] + 2 * d0);
             {
                 const float inv_gv = 1.0f / pp.g_v;
                 float x[4][16];
