@@ -53,8 +53,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 struct QdqSmem {
     uint16_t kt[kTile * kPitch];   // K tile: latent (fp16 or bf16) then RoPE (bf16)
     uint16_t vt[kTile * kPitch];   // V tile: latent (fp16 or bf16)
-    int64_t offs[2][kTile];        // record byte offsets of tiles t, t+1 (masked tokens: 0)
-    uint32_t valid[2];             // bit i: token i of the tile is unmasked
+    u32x4 qs[kWaves][18][64];      // each wavefront's Q B-operand fragments (k-step, lane)
+    int64_t offs[3][kTile];        // record byte offsets of tiles t .. t+2 (masked tokens: 0)
+    uint32_t valid[3];             // bit i: token i of the tile is unmasked
 };
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     // 17: RoPE).  Quantized: NVFP4 blocks of 16 features (block 2kk + gq/2
     // spans lanes gq and gq ^ 1) or per-tensor FP8, the exact values kept.
     // Raw with fp16 K: scaled by 2^(14 - E) per head (exact).
-    u32x4 qf[18];
+    // (held in LDS, sm.qs: the registers go to the staged records)
     float q_mul_lat = 1.0f, q_mul_rope = 1.0f;
     {
         const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(hok ? hq : 0) * p.q_stride_h + 8 * gq;
@@ -204,9 +205,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 for (int i = 0; i < 8; ++i) x[kk][i] = __builtin_ldexpf(x[kk][i], 14 - E);
         }
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) qf[kk] = pack8_exact<kKF16>(x[kk]);
+        for (int kk = 0; kk < 16; ++kk) sm.qs[w][kk][lane] = pack8_exact<kKF16>(x[kk]);
 #pragma unroll
-        for (int kk = 16; kk < 18; ++kk) qf[kk] = pack8_exact<false>(x[kk]);
+        for (int kk = 16; kk < 18; ++kk) sm.qs[w][kk][lane] = pack8_exact<false>(x[kk]);
     }
     // multipliers of the stored operands: NVFP4 latent * outer; raw K or V
     // quantized * g_k, g_v; P quantized * g_p
@@ -223,9 +224,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     const uint8_t* __restrict__ cache = p.cache;
-    // Page walk of tile t into offset slot t % 2 by threads 0..31: the page-
-    // table entry is requested at the start of the previous tile and the
-    // offset stored at its end, so that the load overlaps that tile's work.
+    // Page walk of tile t into offset slot t % 3 by threads 0..31, two tiles
+    // ahead: the page-table entry of tile t + 2 is requested at the start of
+    // tile t and its offsets stored at the end, so that the load overlaps the
+    // tile's work; a raw cache's K words of tile t + 1 are loaded during tile
+    // t's products (registers kw).
+    constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + 255) / 256;   // K: 32 tokens x 36 blocks of 16 features
+    u32x4 kw[kKIt][2];
+    auto load_k_raw = [&](const int64_t* offs) {
+        // (indices clamped, so every address is a record of the tile)
+#pragma unroll
+        for (int j = 0; j < kKIt; ++j) {
+            const int i = min(tid + 256 * j, kKBlk - 1);
+            const u32x4* src = reinterpret_cast<const u32x4*>(cache + offs[i / 36] + 32 * (i % 36));
+            kw[j][0] = src[0];
+            kw[j][1] = src[1];
+        }
+    };
     int pg_next = -1;
     auto walk_request = [&](int t) {
         const int pos = i0 + kTile * t + tid;
@@ -242,18 +257,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             off = ((int64_t)pg_next * p.page_size + rem) * kRec;
         }
         const uint64_t vm = __ballot(off >= 0);
-        sm.offs[t & 1][tid] = off < 0 ? 0 : off;
-        if (tid == 0) sm.valid[t & 1] = (uint32_t)vm;
+        sm.offs[t % 3][tid] = off < 0 ? 0 : off;
+        if (tid == 0) sm.valid[t % 3] = (uint32_t)vm;
     };
     if (tid < kTile && ntiles > 0) {
         walk_request(0);
         walk_store(0);
+        walk_request(1);
+        walk_store(1);
     }
     __syncthreads();
+    if constexpr (kRaw) {
+        if (ntiles > 0) load_k_raw(sm.offs[0]);
+    }
     for (int t = 0; t < ntiles; ++t) {
-        if (tid < kTile) walk_request(t + 1);
-        const int64_t* offs = sm.offs[t & 1];
-        const uint32_t vmask = sm.valid[t & 1];
+        if (tid < kTile) walk_request(t + 2);
+        const int64_t* offs = sm.offs[t % 3];
+        const uint32_t vmask = sm.valid[t % 3];
         // ---- staging
         if constexpr (!kRaw) {
             // 32 tokens x 64 chunks of 8 latent elements: code word + block scale
@@ -291,19 +311,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             }
         } else {
             // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE),
-            // V: 2 blocks of 16 tokens (absolute positions base, base + 16) x
-            // 128 groups of 4 dims.  All K loads are issued before any is
-            // used (indices clamped, so every address is a record of the
-            // tile), then all V loads.
-            constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + 255) / 256;
-            u32x4 kw[kKIt][2];
-#pragma unroll
-            for (int j = 0; j < kKIt; ++j) {
-                const int i = min(tid + 256 * j, kKBlk - 1);
-                const u32x4* src = reinterpret_cast<const u32x4*>(cache + offs[i / 36] + 32 * (i % 36));
-                kw[j][0] = src[0];
-                kw[j][1] = src[1];
-            }
+            // loaded during the previous tile; V: 2 blocks of 16 tokens
+            // (absolute positions base, base + 16) x 128 groups of 4 dims,
+            // all loads issued before any is used.
             const int half = tid >> 7, d0 = 4 * (tid & 127);
             const float inv_gk = 1.0f / pp.g_k;
 #pragma unroll
@@ -366,6 +376,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             }
         }
         __syncthreads();
+        if constexpr (kRaw) {
+            if (t + 1 < ntiles) load_k_raw(sm.offs[(t + 1) % 3]);   // lands during this tile's products
+        }
 
         // ---- S^T = K Q^T: rows 16tt + c16 (tokens), latent and RoPE apart
         f32x4 sl[2], sr[2];
@@ -376,12 +389,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
         }
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) {
+            const u32x4 qv = sm.qs[w][kk][lane];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.kt[(16 * tt + c16) * kPitch + 32 * kk + 8 * gq]);
-                if (kk >= 16) sr[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[kk]), sr[tt]);
-                else if (kKF16) sl[tt] = mfma_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, qf[kk]), sl[tt]);
-                else sl[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[kk]), sl[tt]);
+                if (kk >= 16) sr[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qv), sr[tt]);
+                else if (kKF16) sl[tt] = mfma_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, qv), sl[tt]);
+                else sl[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qv), sl[tt]);
             }
         }
         // ---- softmax (log2 units): token 16tt + 4gq + i of head c16
@@ -497,7 +511,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 for (int c = 0; c < 32; ++c) o[c] = mfma16x16x32(as_bf16x8(vt_frag(c)), bp, o[c]);
             }
         }
-        if (tid < kTile) walk_store(t + 1);
+        if (tid < kTile) walk_store(t + 2);
         __syncthreads();   // the tiles are restaged next iteration
     }
 
