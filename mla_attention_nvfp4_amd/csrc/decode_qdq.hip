@@ -119,9 +119,26 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     const DecodeArgs& p = pp.d;
     __shared__ QdqSmem sm;
 
-    int s, u;
-    decode_work_item(p.max_splits, p.B * (int)gridDim.z, s, u);
-    const int b = u % p.B, hg = u / p.B;
+    // Placement: workgroups are dispatched round-robin over the 8 XCDs in
+    // linear-id order.  When 8 divides B, sequence b runs on XCD b % 8 and the
+    // head groups of one (sequence, split) are consecutive there, so that
+    // they run together and all but the first read the records from that
+    // XCD's L2 (a bijection onto splits x sequences x head groups).
+    int s, b, hg;
+    {
+        const int G = (int)gridDim.z, S = p.max_splits;
+        const int L = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+        if ((p.B & 7) == 0) {
+            const int k = L >> 3;
+            hg = k % G;
+            s = (k / G) % S;
+            b = (L & 7) + 8 * (k / (G * S));
+        } else {
+            hg = L % G;
+            s = (L / G) % S;
+            b = L / (G * S);
+        }
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int gq = lane >> 4, c16 = lane & 15;
