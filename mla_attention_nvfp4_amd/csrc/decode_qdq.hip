@@ -15,15 +15,18 @@
 // wavefronts, each owning 16 heads.  The split's tokens are walked in tiles
 // of 32; every wavefront sees all of them in order, so each holds one
 // running max, refreshed per tile, against which P is quantized.  Per tile:
-//   offsets   threads 0..31 walk the page table for the tile's tokens;
+//   offsets   threads 0..31 walk the page table two tiles ahead (three
+//             offset slots in LDS);
 //   staging   the workgroup dequantizes (NVFP4 records: s*v, exact in fp16)
 //             or quantizes (raw records: K in 16-feature blocks, V in
 //             16-token blocks per dim, from the bf16 values) the tile into a
 //             K tile (576 columns; RoPE columns bf16) and a V tile (512
-//             columns) in LDS;
-//   compute   S^T = K Q^T on v_mfma_f32_16x16x32 (latent k-steps fp16, or
-//             bf16 for raw unquantized K; RoPE k-steps bf16), latent and RoPE
-//             partial scores scaled separately; online softmax in base 2;
+//             columns) in LDS; a raw tile's K words are loaded during the
+//             previous tile's products;
+//   compute   S^T = K Q^T on v_mfma_f32_16x16x32 (Q's fragments in LDS;
+//             latent k-steps fp16, or bf16 for raw unquantized K; RoPE
+//             k-steps bf16), latent and RoPE partial scores scaled
+//             separately; online softmax in base 2;
 //             P quantized per 16-key block (NVFP4) or per element (FP8),
 //             exact in the fp16 / bf16 B operand, or unquantized as fp16
 //             hi + lo (bf16 V: three bf16 parts); O^T = V^T P^T with V^T
