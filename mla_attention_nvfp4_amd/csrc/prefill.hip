@@ -275,13 +275,15 @@ struct BoolTag {
 };
 
 // Layout of a wavefront's work on one 64-key tile (32 query rows): lane l
-// owns query row l % 32 (g2 = l / 32 picks half of the keys).  Score tile
-// mt2 = S^T for keys 32 mt2 .. +31; its element v is key 32 mt2 + 8(v/4) +
-// 4 g2 + v%4.  So the 16-key P block kb (keys 16kb .. +15) is elements
-// 8(kb%2) .. +7 of tile kb/2 in lanes l and l ^ 32, and those 8 values, in
-// order, are also the k-slots of k-step kb of the B operand of O^T = V^T P^T
-// (slot j <-> key 16kb + 8(j/4) + 4 g2 + j%4; the V^T operand uses the same
-// slots).
+// owns query row l % 32 (g2 = l / 32 picks half of the keys).  K and V tile
+// rows are stored permuted: within each 32-key half, LDS row 8a + 4g + b
+// holds key 16g + 4a + b (tile_row below).  Score tile mt2 = S^T for the
+// rows 32 mt2 .. +31; its element v is row 32 mt2 + 8(v/4) + 4 g2 + v%4,
+// which holds key 32 mt2 + 16 g2 + v.  So a lane's 16 elements of tile mt2
+// are one whole 16-key P block (keys 32 mt2 + 16 g2 .. +15, block 2 mt2 + g2)
+// in order, and elements 8h .. 8h+7 of tile mt2 are also the k-slots of
+// k-step 2 mt2 + h of the B operand of O^T = V^T P^T (slot j <-> row
+// 32 mt2 + 16h + 8(j/4) + 4 g2 + j%4; the V^T operand reads the same rows).
 //
 // kPMode: 0 P unquantized, 1 NVFP4 blocks along keys, 2 per-tensor FP8.
 // kF16: P and V are both quantized, so P^ (s*v or an e4m3 value) and V^ are
@@ -408,17 +410,26 @@ void attn_kernel(AttnParams p) {
             }
         }
     };
+    // LDS row of tile key k: within its 32-key half, key 16g + 4a + b goes
+    // to row 8a + 4g + b (the layout described above the kernel)
+    // (each thread's store offsets are the same for every tile)
+    auto tile_row = [](int k) { return (k & 32) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3); };
+    int kso[3], vso[2];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int c = tid + 512 * i;
+        kso[i] = tile_row(c / 24) * kPitchK + 8 * (c % 24);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 512 * i;
+        vso[i] = tile_row(c >> 4) * kPitchV + 8 * (c & 15);
+    }
     auto store_tile = [&](int buf, int vbuf) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int c = tid + 512 * i;
-            *reinterpret_cast<u32x4*>(&sm.kt[buf][(c / 24) * kPitchK + 8 * (c % 24)]) = sk[i];
-        }
+        for (int i = 0; i < 3; ++i) *reinterpret_cast<u32x4*>(&sm.kt[buf][kso[i]]) = sk[i];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 512 * i;
-            *reinterpret_cast<u32x4*>(&sm.vt[vbuf][(c >> 4) * kPitchV + 8 * (c & 15)]) = sv[i];
-        }
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sm.vt[vbuf][vso[i]]) = sv[i];
     };
 
     f32x16 o[4];   // O^T: element v of o[dt] is dim 32dt + 8(v/4) + 4 g2 + v%4 of this row
@@ -431,10 +442,10 @@ void attn_kernel(AttnParams p) {
     // wavefronts 4-7 keep it for one iteration when the PV is deferred
     f16x8 hold[4];
     // O^T += V^T P^T.  A fragment (dim tile dt, k-step kb) of the V tile at
-    // vb: lane l gets dim 32dt + l%32 and keys 16kb + 4 g2 + 0..3 (slots
+    // vb: lane l gets dim 32dt + l%32 and rows 16kb + 4 g2 + 0..3 (slots
     // 0..3) and 16kb + 8 + 4 g2 + 0..3 (slots 4..7) by two transposing reads;
-    // in each 16-lane group lane s addresses key row k0 + s/4 and dims c0 +
-    // 4(s%4) .. +3, and receives the 4 keys of dim c0 + s.
+    // in each 16-lane group lane s addresses row k0 + s/4 and dims c0 +
+    // 4(s%4) .. +3, and receives the 4 rows of dim c0 + s.
     const int s16 = lane & 15;
     const int vlane = (4 * g2 + (s16 >> 2)) * kPitchV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
     auto vfrag = [&](const uint16_t* vb, int kb, int dt) {
@@ -491,8 +502,8 @@ void attn_kernel(AttnParams p) {
         // since fp32(c x) is monotone in x for c >= 0, and each exponent is
         // one fused c * s - m)
         float mx = -INFINITY;
-        // element v of score tile mt2 is key 32 mt2 + 8 (v / 4) + v % 4 of
-        // this lane's quarter of the tile; with 2:4 sparsity, of each group
+        // element v of score tile mt2 is key 32 mt2 + 16 g2 + v of the tile
+        // (the permuted rows above); with 2:4 sparsity, of each group
         // of 4 keys (elements 4c .. 4c+3) the two outranked by two others are
         // dropped: key i beats key j > i when x_i >= x_j (equal scores rank
         // by index), one comparison per pair
@@ -509,14 +520,14 @@ void attn_kernel(AttnParams p) {
             // keys past this row's last key are masked; the 2:4 ranking sees
             // them as -inf and ranks the raw scores (times rank_mul: 0 when
             // softmax_scale is 0, which makes every seen score tie)
-            const int rel = lim - (kt * kBN + 4 * g2);   // last key offset this lane's row sees
+            const int rel = lim - (kt * kBN + 16 * g2);  // last key offset this lane's row sees
 #pragma unroll
             for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     bool seen[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) seen[i] = 32 * mt2 + 8 * c + i <= rel;
+                    for (int i = 0; i < 4; ++i) seen[i] = 32 * mt2 + 4 * c + i <= rel;
                     if constexpr (kSparse) {
                         float x[4];
 #pragma unroll
@@ -602,38 +613,41 @@ void attn_kernel(AttnParams p) {
                 }
             }
         } else if constexpr (kQuantP) {
-            // block amax, then the four blocks' scales side by side (the rare
-            // exact divisions in one uniform branch)
-            float am[4], tq[4];
-            bool nr[4];
+            // this lane's two P blocks (elements 0..15 of s[mt2], block
+            // 2 mt2 + g2): maxima and scales side by side (the rare exact
+            // divisions in one uniform branch)
+            float am[2], tq[2];
+            bool nr[2];
             bool any_near = false;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const f32x16& t = s[kb >> 1];
-                const int o8 = 8 * (kb & 1);
-                am[kb] = fmaxf(fmaxf(fmaxf(t[o8], t[o8 + 1]), fmaxf(t[o8 + 2], t[o8 + 3])),
-                               fmaxf(fmaxf(t[o8 + 4], t[o8 + 5]), fmaxf(t[o8 + 6], t[o8 + 7])));
-            }
+            for (int mt2 = 0; mt2 < 2; ++mt2) {
+                const f32x16& t = s[mt2];
+                float m8[2];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                am[kb] = xor32_max(am[kb]);
-                tq[kb] = am[kb] * p.inv_u_p;
-                nr[kb] = scale_quotient_near_tie(tq[kb]);
-                any_near |= nr[kb];
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int o8 = 8 * hh;
+                    m8[hh] = fmaxf(fmaxf(fmaxf(t[o8], t[o8 + 1]), fmaxf(t[o8 + 2], t[o8 + 3])),
+                                   fmaxf(fmaxf(t[o8 + 4], t[o8 + 5]), fmaxf(t[o8 + 6], t[o8 + 7])));
+                }
+                am[mt2] = fmaxf(m8[0], m8[1]);
+                tq[mt2] = am[mt2] * p.inv_u_p;
+                nr[mt2] = scale_quotient_near_tie(tq[mt2]);
+                any_near |= nr[mt2];
             }
             if (__any(any_near)) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) tq[kb] = nr[kb] ? am[kb] / p.u_p : tq[kb];
+                for (int mt2 = 0; mt2 < 2; ++mt2) tq[mt2] = nr[mt2] ? am[mt2] / p.u_p : tq[mt2];
             }
-            // the four blocks' e4m3 codes by two hardware conversions (tq >= 0;
+            // the two blocks' e4m3 codes by one hardware conversion (tq >= 0;
             // see e4m3_encode_nonneg)
-            uint32_t codes4 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(tq[0], 448.0f), fminf(tq[1], 448.0f), 0, false);
-            codes4 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(tq[2], 448.0f), fminf(tq[3], 448.0f), (int)codes4, true);
+            const uint32_t codes2 =
+                (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(tq[0], 448.0f), fminf(tq[1], 448.0f), 0, false);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
+                // k-step kb: elements 8(kb%2) .. +7 of s[kb/2], block kb/2's scale
                 const f32x16& t = s[kb >> 1];
                 const int o8 = 8 * (kb & 1);
-                const uint32_t code = (codes4 >> (8 * kb)) & 0xffu;
+                const uint32_t code = (codes2 >> (8 * (kb >> 1))) & 0xffu;
                 const float inv = sm.pinv[code];
                 const float sval = e4m3_decode(code);
                 uint32_t c8 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[o8] * inv, t[o8 + 1] * inv, 1.0f, 0);
