@@ -48,7 +48,7 @@ typedef enum {
     MLA_ERR_UNSUPPORTED_DEVICE = -3, /* current device is not gfx950 */
     MLA_ERR_WORKSPACE_TOO_SMALL = -4,
     MLA_ERR_HIP = -5,                /* a HIP runtime call failed */
-    MLA_ERR_UNSUPPORTED = -6         /* valid request this build cannot serve */
+    MLA_ERR_UNSUPPORTED = -6         /* valid request the library does not serve */
 } mla_status;
 
 /* Fixed geometry of the latent ([MO-MLA], PR body: absorbed decode over a
