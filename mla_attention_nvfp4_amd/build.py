@@ -34,6 +34,10 @@ CFLAGS = [
 # and the loop-carried accumulators are not copied between register files.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "decode_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # MFMA rate loops: with AGPR accumulators the compiler copies the
+         # loop-carried accumulators between register files every iteration,
+         # which would time the copies instead of the products
+         "roofline.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          # prefill: inputs are finite, so the max reductions of the softmax and
          # the P blocks need no NaN canonicalization (about 12% of the
          # attention loop's VALU instructions)
