@@ -651,10 +651,23 @@ __device__ __forceinline__ float wave_sum64(float v) {
 
 template <bool kSparse>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // Workgroup: sequence b, heads 4hq..4hq+3.  When B is a multiple of 8,
+    // sequence b's workgroups are placed on XCD b % 8, where the decode
+    // kernels ran all of its splits, so the partials are read from the L2
+    // they were written to (a bijection; otherwise the identity).
+    const int HQ = (p.H + 3) / 4, L = (int)blockIdx.x;
+    int b, hq;
+    if ((p.B & 7) == 0) {
+        const int k = L >> 3;
+        b = (L & 7) + 8 * (k / HQ);
+        hq = k % HQ;
+    } else {
+        b = L / HQ;
+        hq = L % HQ;
+    }
+    const int h = 4 * hq + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (wid >= p.B * p.H) return;
-    const int b = wid / p.H, h = wid % p.H;
+    if (h >= p.H) return;
     const int64_t row0 = (int64_t)b * p.max_splits * p.H + h;   // split s at row0 + s*H
     float* dst = p.out + ((int64_t)b * p.H + h) * kLatent + 8 * lane;
     const int64_t rl = row0 + (int64_t)(lane < p.max_splits ? lane : 0) * p.H;
@@ -844,11 +857,11 @@ hipError_t launch_decode_pq(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t waves = (int64_t)a.B * a.H;
+    const int64_t blocks = (int64_t)a.B * ((a.H + 3) / 4);   // (sequence, 4 heads)
     if (a.indices)
-        hipLaunchKernelGGL((split_merge_kernel<true>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_merge_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((split_merge_kernel<false>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_merge_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -23,6 +23,11 @@ SMALL_DENSE = [
     (10, 2, 100, [555, 1200], 64, 368, 1.1, 2),       # wide, partial head group
     (16, 2, 256, [700, 1500], 64, 432, 1.2, 3),       # two 128-head groups
     (17, 1, 300, [400], 16, 368, 0.9, 2),             # three head groups, the last partial
+    # batches of 8 (the split merge then runs sequence b on XCD b % 8) with
+    # head counts that leave the merge's last group of 4 heads partial
+    (19, 8, 15, [0, 1, 65, 300, 129, 700, 33, 256], 16, 432, 1.0, 3),
+    (20, 8, 130, [64, 700, 1, 300, 0, 257, 900, 40], 64, 368, 0.8, 3),
+    (23, 16, 17, [300, 5, 129, 64, 700, 1, 0, 200, 33, 256, 513, 90, 64, 128, 31, 400], 48, 432, 1.1, 2),
 ]
 
 
@@ -96,6 +101,7 @@ SMALL_SPARSE = [
     (13, 2, 128, [5000, 3000], 512, 0.1, 4),
     (14, 2, 48, [64, 300], 130, 0.5, 3),
     (18, 2, 256, [3000, 800], 300, 0.1, 2),           # two 128-head groups
+    (24, 8, 18, [900, 100, 0, 600, 2000, 64, 300, 1200], 260, 0.1, 3),   # batch of 8, 18 heads
 ]
 
 
