@@ -655,15 +655,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
     // sequence b's workgroups are placed on XCD b % 8, where the decode
     // kernels ran all of its splits, so the partials are read from the L2
     // they were written to (a bijection; otherwise the identity).
-    const int HQ = (p.H + 3) / 4, L = (int)blockIdx.x;
+    const int HQ = (p.H + 3) / 4, wg = (int)blockIdx.x;
     int b, hq;
     if ((p.B & 7) == 0) {
-        const int k = L >> 3;
-        b = (L & 7) + 8 * (k / HQ);
+        const int k = wg >> 3;
+        b = (wg & 7) + 8 * (k / HQ);
         hq = k % HQ;
     } else {
-        b = L / HQ;
-        hq = L % HQ;
+        b = wg / HQ;
+        hq = wg % HQ;
     }
     const int h = 4 * hq + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
