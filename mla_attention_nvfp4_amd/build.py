@@ -34,6 +34,7 @@ CFLAGS = [
 # and the loop-carried accumulators are not copied between register files.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "decode_narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_qdq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          # MFMA rate loops: with AGPR accumulators the compiler copies the
          # loop-carried accumulators between register files every iteration,
          # which would time the copies instead of the products

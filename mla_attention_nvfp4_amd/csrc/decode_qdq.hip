@@ -11,10 +11,11 @@
 // per-tensor FP8 per operand, as in the prefill.  [B12X], walkthrough: the
 // NVFP4 records are dequantized on read with the per-layer outer scale.
 //
-// Work item: workgroup (split s, sequence b, group of 64 heads) of 4
-// wavefronts, each owning 16 heads.  The split's tokens are walked in tiles
-// of 32; every wavefront sees all of them in order, so each holds one
-// running max, refreshed per tile, against which P is quantized.  Per tile:
+// Work item: workgroup (split s, sequence b, group of 128 heads) of 8
+// wavefronts (two per SIMD), each owning 16 heads, so that a tile is staged
+// once for all 128 heads.  The split's tokens are walked in tiles of 32;
+// every wavefront sees all of them in order, so each holds one running max,
+// refreshed per tile, against which P is quantized.  Per tile:
 //   offsets   threads 0..31 walk the page table two tiles ahead (three
 //             offset slots in LDS);
 //   staging   the workgroup dequantizes (NVFP4 records: s*v, exact in fp16)
@@ -22,11 +23,14 @@
 //             16-token blocks per dim, from the bf16 values) the tile into a
 //             K tile (576 columns; RoPE columns bf16) and a V tile (512
 //             columns) in LDS; a raw tile's K words are loaded during the
-//             previous tile's products;
-//   compute   S^T = K Q^T on v_mfma_f32_16x16x32 (Q's fragments in LDS;
-//             latent k-steps fp16, or bf16 for raw unquantized K; RoPE
-//             k-steps bf16), latent and RoPE partial scores scaled
-//             separately; online softmax in base 2;
+//             previous tile's softmax and PV products;
+//   compute   (wavefronts that own heads) S^T = K Q^T on
+//             v_mfma_f32_16x16x32 (Q's first kQLdsLatent latent k-steps and
+//             its RoPE k-steps in LDS, the others in registers; latent
+//             k-steps fp16, or bf16 for raw unquantized K; RoPE k-steps
+//             bf16), fragments one k-step ahead of their products, latent
+//             and RoPE partial scores scaled separately; online softmax in
+//             base 2;
 //             P quantized per 16-key block (NVFP4) or per element (FP8),
 //             exact in the fp16 / bf16 B operand, or unquantized as fp16
 //             hi + lo (bf16 V: three bf16 parts); O^T = V^T P^T with V^T
@@ -43,8 +47,14 @@ namespace {
 
 constexpr int kTile = 32;
 constexpr int kPitch = kQK + 16;   // elements per tile row (592: 1184 B, conflict-free fragment reads)
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kHeadsPerGroup = 16 * kWaves;
+// Q k-steps kept in LDS (B-operand layout, 16 B per lane): the first
+// kQLdsLatent latent k-steps and the two RoPE k-steps; the others stay in
+// registers.
+constexpr int kQLdsLatent = 6;
+constexpr int kQLds = kQLdsLatent + 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -56,7 +66,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 struct QdqSmem {
     uint16_t kt[kTile * kPitch];   // K tile: latent (fp16 or bf16) then RoPE (bf16)
     uint16_t vt[kTile * kPitch];   // V tile: latent (fp16 or bf16)
-    u32x4 qs[kWaves][18][64];      // each wavefront's Q B-operand fragments (k-step, lane)
+    u32x4 qs[kWaves][kQLds][64];   // each wavefront's LDS-held Q B-operand fragments (slot, lane)
     int64_t offs[3][kTile];        // record byte offsets of tiles t .. t+2 (masked tokens: 0)
     uint32_t valid[3];             // bit i: token i of the tile is unmasked
 };
@@ -116,7 +126,8 @@ struct QdqParams {
 // records (1152 B).  kKF16 / kVF16: the latent K / V tile holds fp16 (exact
 // s*v or e4m3 values) rather than bf16 (raw values).
 template <int kCache, bool kKF16, bool kVF16>
-__global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_qdq_kernel(QdqParams pp) {
     constexpr bool kRaw = kCache == 2;
     constexpr int kRec = kCache == 0 ? 432 : (kCache == 1 ? 368 : 1152);
     const DecodeArgs& p = pp.d;
@@ -147,6 +158,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     const int gq = lane >> 4, c16 = lane & 15;
     const int hq = hg * kHeadsPerGroup + 16 * w + c16;
     const bool hok = hq < p.H;
+    const bool wave_active = hg * kHeadsPerGroup + 16 * w < p.H;   // (wavefront-uniform)
 
     int L = p.seq_lens[b];
     const int Lmax = p.max_pages * p.page_size;
@@ -165,8 +177,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     // 17: RoPE).  Quantized: NVFP4 blocks of 16 features (block 2kk + gq/2
     // spans lanes gq and gq ^ 1) or per-tensor FP8, the exact values kept.
     // Raw with fp16 K: scaled by 2^(14 - E) per head (exact).
-    // (held in LDS, sm.qs: the registers go to the staged records)
+    // (k-steps kQLdsLatent..15 in registers qf, the others in LDS sm.qs)
     float q_mul_lat = 1.0f, q_mul_rope = 1.0f;
+    u32x4 qf[16 - kQLdsLatent];
     {
         const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(hok ? hq : 0) * p.q_stride_h + 8 * gq;
         const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -225,9 +238,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 for (int i = 0; i < 8; ++i) x[kk][i] = __builtin_ldexpf(x[kk][i], 14 - E);
         }
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) sm.qs[w][kk][lane] = pack8_exact<kKF16>(x[kk]);
+        for (int kk = 0; kk < 16; ++kk) {
+            if (kk < kQLdsLatent) sm.qs[w][kk][lane] = pack8_exact<kKF16>(x[kk]);
+            else qf[kk - kQLdsLatent] = pack8_exact<kKF16>(x[kk]);
+        }
 #pragma unroll
-        for (int kk = 16; kk < 18; ++kk) sm.qs[w][kk][lane] = pack8_exact<false>(x[kk]);
+        for (int kk = 16; kk < 18; ++kk) sm.qs[w][kQLdsLatent + kk - 16][lane] = pack8_exact<false>(x[kk]);
     }
     // multipliers of the stored operands: NVFP4 latent * outer; raw K or V
     // quantized * g_k, g_v; P quantized * g_p
@@ -249,13 +265,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
     // tile t and its offsets stored at the end, so that the load overlaps the
     // tile's work; a raw cache's K words of tile t + 1 are loaded during tile
     // t's products (registers kw).
-    constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + 255) / 256;   // K: 32 tokens x 36 blocks of 16 features
+    constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + kThreads - 1) / kThreads;   // K: 32 tokens x 36 blocks of 16 features
     u32x4 kw[kKIt][2];
     auto load_k_raw = [&](const int64_t* offs) {
         // (indices clamped, so every address is a record of the tile)
 #pragma unroll
         for (int j = 0; j < kKIt; ++j) {
-            const int i = min(tid + 256 * j, kKBlk - 1);
+            const int i = min(tid + kThreads * j, kKBlk - 1);
             const u32x4* src = reinterpret_cast<const u32x4*>(cache + offs[i / 36] + 32 * (i % 36));
             kw[j][0] = src[0];
             kw[j][1] = src[1];
@@ -298,8 +314,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
         if constexpr (!kRaw) {
             // 32 tokens x 64 chunks of 8 latent elements: code word + block scale
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = tid + 256 * k;
+            for (int k = 0; k < 2048 / kThreads; ++k) {
+                const int c = tid + kThreads * k;
                 const int tok = c >> 6, ch = c & 63;
                 const uint8_t* rp = cache + offs[tok];
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(rp + 4 * ch);
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 *reinterpret_cast<u32x4*>(&sm.kt[tok * kPitch + 8 * ch]) = wv;
                 *reinterpret_cast<u32x4*>(&sm.vt[tok * kPitch + 8 * ch]) = wv;
             }
-            {   // RoPE: 32 tokens x 8 units of 8 values
+            if (tid < 256) {   // RoPE: 32 tokens x 8 units of 8 values
                 const int tok = tid >> 3, un = tid & 7;
                 const uint8_t* rp = cache + offs[tok];
                 u32x4 wv;
@@ -332,13 +348,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
         } else {
             // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE),
             // loaded during the previous tile; V: 2 blocks of 16 tokens
-            // (absolute positions base, base + 16) x 128 groups of 4 dims,
+            // (absolute positions base, base + 16) x 256 pairs of dims,
             // all loads issued before any is used.
-            const int half = tid >> 7, d0 = 4 * (tid & 127);
+            const int half = tid >> 8, d0 = 2 * (tid & 255);
             const float inv_gk = 1.0f / pp.g_k;
 #pragma unroll
             for (int j = 0; j < kKIt; ++j) {
-                const int i = tid + 256 * j;
+                const int i = tid + kThreads * j;
                 if (i >= kKBlk) break;
                 const int tok = i / 36, blk = i % 36;
                 const bool ok = (vmask >> tok) & 1u;
@@ -365,41 +381,34 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
                 dst[1] = c;
             }
             // V: per dim the block's amax (NVFP4) or each element (FP8)
-            u32x2 vr[16];
+            uint32_t vr[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const u32x2*>(cache + offs[16 * half + i] + 2 * d0);
+            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(cache + offs[16 * half + i] + 2 * d0);
             {
                 const float inv_gv = 1.0f / pp.g_v;
-                float x[4][16];
+                float x[2][16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tok = 16 * half + i;
                     const bool ok = (vmask >> tok) & 1u;
-                    const u32x2 r = vr[i];
-                    x[0][i] = ok ? bf16_lo(r[0]) : 0.0f;
-                    x[1][i] = ok ? bf16_hi(r[0]) : 0.0f;
-                    x[2][i] = ok ? bf16_lo(r[1]) : 0.0f;
-                    x[3][i] = ok ? bf16_hi(r[1]) : 0.0f;
+                    x[0][i] = ok ? bf16_lo(vr[i]) : 0.0f;
+                    x[1][i] = ok ? bf16_hi(vr[i]) : 0.0f;
                 }
                 if (qV) {
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) qdq16(x[d], fV, pp.g_v, inv_gv);
+                    for (int d = 0; d < 2; ++d) qdq16(x[d], fV, pp.g_v, inv_gv);
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tok = 16 * half + i;
-                    u32x2 wv;
-                    if (kVF16) wv = u32x2{pack_f16(x[0][i], x[1][i]), pack_f16(x[2][i], x[3][i])};
-                    else wv = u32x2{pack_bf16_exact(x[0][i], x[1][i]), pack_bf16_exact(x[2][i], x[3][i])};
-                    *reinterpret_cast<u32x2*>(&sm.vt[tok * kPitch + d0]) = wv;
+                    *reinterpret_cast<uint32_t*>(&sm.vt[tok * kPitch + d0]) =
+                        kVF16 ? pack_f16(x[0][i], x[1][i]) : pack_bf16_exact(x[0][i], x[1][i]);
                 }
             }
         }
         __syncthreads();
-        if constexpr (kRaw) {
-            if (t + 1 < ntiles) load_k_raw(sm.offs[(t + 1) % 3]);   // lands during this tile's products
-        }
 
+        // (wavefronts past the last head only stage and prefetch)
         // ---- S^T = K Q^T: rows 16tt + c16 (tokens), latent and RoPE apart
         f32x4 sl[2], sr[2];
 #pragma unroll
@@ -407,128 +416,177 @@ __global__ __launch_bounds__(kWaves * 64) void decode_qdq_kernel(QdqParams pp) {
             sl[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             sr[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        if (wave_active) {
+            // fragments (and LDS-held Q) one k-step ahead of their MFMAs
+            auto q_lds = [](int kk) { return kk < kQLdsLatent || kk >= 16; };
+            auto q_slot = [](int kk) { return kk < 16 ? kk : kQLdsLatent + kk - 16; };
+            auto kt_frag = [&](int kk, int tt) {
+                return *reinterpret_cast<const u32x4*>(&sm.kt[(16 * tt + c16) * kPitch + 32 * kk + 8 * gq]);
+            };
+            u32x4 f0[2], f1[2], qb[2];
+            f0[0] = kt_frag(0, 0);
+            f1[0] = kt_frag(0, 1);
+            qb[0] = sm.qs[w][q_slot(0)][lane];
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-            const u32x4 qv = sm.qs[w][kk][lane];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&sm.kt[(16 * tt + c16) * kPitch + 32 * kk + 8 * gq]);
-                if (kk >= 16) sr[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qv), sr[tt]);
-                else if (kKF16) sl[tt] = mfma_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, qv), sl[tt]);
-                else sl[tt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qv), sl[tt]);
-            }
-        }
-        // ---- softmax (log2 units): token 16tt + 4gq + i of head c16
-        float z[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * tt + 4 * gq + i;
-                z[tt][i] = ((vmask >> tok) & 1u) ? sc_lat * sl[tt][i] + sc_rope * sr[tt][i] : -INFINITY;
-                mx = fmaxf(mx, z[tt][i]);
-            }
-        mx = xor32_max(xor16_max(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        float pv[2][4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[tt][i] = __builtin_amdgcn_exp2f(z[tt][i] - m_use);   // masked: 0
-                psum += pv[tt][i];
-            }
-        psum = xor32_sum(xor16_sum(psum));
-        l_run = alpha * l_run + psum;   // unquantized denominator
-        m_run = m_new;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int c = 0; c < 32; ++c) o[c] *= alpha;
-        }
-        // ---- P (B operand; k-slot j < 4: token 4gq + j, j >= 4: token
-        // 16 + 4gq + j - 4).  P block tt (16 keys) of head c16: this lane's 4
-        // values and those of lanes c16 + 16g'.
-        float ph[2][4], pm[2][4], plo[2][4];
-        int sweeps = 1;
-        if (qP) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                if (fP) {
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const uint32_t c2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-                            fminf(pv[tt][i] * inv_g_p, 448.0f), fminf(pv[tt][i + 1] * inv_g_p, 448.0f), 0, false);
-                        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
-                        ph[tt][i] = d[0];
-                        ph[tt][i + 1] = d[1];
-                    }
-                } else {
-                    float a = fmaxf(fmaxf(pv[tt][0], pv[tt][1]), fmaxf(pv[tt][2], pv[tt][3]));
-                    a = xor32_max(xor16_max(a));
-                    float tq = a * inv_u_p;
-                    if (scale_quotient_near_tie(tq)) tq = a / u_p;
-                    const uint32_t code = e4m3_encode_nonneg(tq);
-                    const float sv = e4m3_decode(code);
-                    const float dd = sv * pp.g_p;
-                    const float inv = dd == 0.0f ? 0.0f : 1.0f / dd;
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const f32x2 d = e2m1_pair<0>(e2m1_pack2<0>(0u, pv[tt][i] * inv, pv[tt][i + 1] * inv));
-                        ph[tt][i] = d[0] * sv;
-                        ph[tt][i + 1] = d[1] * sv;
-                    }
+            for (int kk = 0; kk < 18; ++kk) {
+                if (kk + 1 < 18) {
+                    f0[(kk + 1) & 1] = kt_frag(kk + 1, 0);
+                    f1[(kk + 1) & 1] = kt_frag(kk + 1, 1);
+                    if (q_lds(kk + 1)) qb[(kk + 1) & 1] = sm.qs[w][q_slot(kk + 1)][lane];
                 }
+                const u32x4 qv = q_lds(kk) ? qb[kk & 1] : qf[kk - kQLdsLatent];
+                const u32x4 a0 = f0[kk & 1], a1 = f1[kk & 1];
+                if (kk >= 16) {
+                    sr[0] = mfma16x16x32(as_bf16x8(a0), as_bf16x8(qv), sr[0]);
+                    sr[1] = mfma16x16x32(as_bf16x8(a1), as_bf16x8(qv), sr[1]);
+                } else if (kKF16) {
+                    sl[0] = mfma_f16(__builtin_bit_cast(f16x8, a0), __builtin_bit_cast(f16x8, qv), sl[0]);
+                    sl[1] = mfma_f16(__builtin_bit_cast(f16x8, a1), __builtin_bit_cast(f16x8, qv), sl[1]);
+                } else {
+                    sl[0] = mfma16x16x32(as_bf16x8(a0), as_bf16x8(qv), sl[0]);
+                    sl[1] = mfma16x16x32(as_bf16x8(a1), as_bf16x8(qv), sl[1]);
+                }
+                if (kk + 1 < 18) {   // the next k-step's reads ahead of this step's products
+                    if (q_lds(kk + 1)) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        } else {
-            // unquantized: fp16 hi + lo (fp16 V), or three bf16 parts (bf16 V)
+        }
+        if constexpr (kRaw) {   // the next tile's K words land during this tile's softmax and PV
+            if (t + 1 < ntiles) load_k_raw(sm.offs[(t + 1) % 3]);
+        }
+        if (wave_active) {
+            // ---- softmax (log2 units): token 16tt + 4gq + i of head c16
+            float z[2][4];
+            float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float x = pv[tt][i];
-                    if (kVF16) {
-                        ph[tt][i] = (float)(_Float16)x;
-                        pm[tt][i] = (float)(_Float16)(x - ph[tt][i]);
-                    } else {
-                        ph[tt][i] = bf16_lo(pack_bf16_rne(x, 0.0f));
-                        const float r = x - ph[tt][i];
-                        pm[tt][i] = bf16_lo(pack_bf16_rne(r, 0.0f));
-                        plo[tt][i] = bf16_lo(pack_bf16_rne(r - pm[tt][i], 0.0f));
-                    }
+                    const int tok = 16 * tt + 4 * gq + i;
+                    z[tt][i] = ((vmask >> tok) & 1u) ? sc_lat * sl[tt][i] + sc_rope * sr[tt][i] : -INFINITY;
+                    mx = fmaxf(mx, z[tt][i]);
                 }
-            sweeps = kVF16 ? 2 : 3;
-        }
-        // ---- O^T += V^T P^T: V^T fragment of column tile c by transposing
-        // reads (tokens 4gq + s/4 and 16 + 4gq + s/4 in each 16-lane group)
-        const uint16_t* vb1 = sm.vt + (4 * gq + (c16 >> 2)) * kPitch + 4 * (c16 & 3);
-        const uint16_t* vb2 = sm.vt + (16 + 4 * gq + (c16 >> 2)) * kPitch + 4 * (c16 & 3);
-        auto vt_frag = [&](int c) {
-            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(vb1 + 16 * c)));
-            const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(vb2 + 16 * c)));
-            const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
-            return u32x4{y1[0], y1[1], y2[0], y2[1]};
-        };
-        for (int sw = 0; sw < sweeps; ++sw) {
-            float pp8[8];
+            mx = xor32_max(xor16_max(mx));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            float pv[2][4];
+            float psum = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pp8[4 * tt + i] = sw == 0 ? ph[tt][i] : (sw == 1 ? pm[tt][i] : plo[tt][i]);
-            if (kVF16) {
-                const f16x8 bp = __builtin_bit_cast(f16x8, u32x4{pack_f16(pp8[0], pp8[1]), pack_f16(pp8[2], pp8[3]),
-                                                                 pack_f16(pp8[4], pp8[5]), pack_f16(pp8[6], pp8[7])});
+                for (int i = 0; i < 4; ++i) {
+                    pv[tt][i] = __builtin_amdgcn_exp2f(z[tt][i] - m_use);   // masked: 0
+                    psum += pv[tt][i];
+                }
+            psum = xor32_sum(xor16_sum(psum));
+            l_run = alpha * l_run + psum;   // unquantized denominator
+            m_run = m_new;
+            if (__any(alpha != 1.0f)) {
 #pragma unroll
-                for (int c = 0; c < 32; ++c) o[c] = mfma_f16(__builtin_bit_cast(f16x8, vt_frag(c)), bp, o[c]);
+                for (int c = 0; c < 32; ++c) o[c] *= alpha;
+            }
+            // ---- P (B operand; k-slot j < 4: token 4gq + j, j >= 4: token
+            // 16 + 4gq + j - 4).  P block tt (16 keys) of head c16: this lane's 4
+            // values and those of lanes c16 + 16g'.
+            float ph[2][4], pm[2][4], plo[2][4];
+            int sweeps = 1;
+            if (qP) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    if (fP) {
+#pragma unroll
+                        for (int i = 0; i < 4; i += 2) {
+                            const uint32_t c2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                                fminf(pv[tt][i] * inv_g_p, 448.0f), fminf(pv[tt][i + 1] * inv_g_p, 448.0f), 0, false);
+                            const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(c2, false);
+                            ph[tt][i] = d[0];
+                            ph[tt][i + 1] = d[1];
+                        }
+                    } else {
+                        float a = fmaxf(fmaxf(pv[tt][0], pv[tt][1]), fmaxf(pv[tt][2], pv[tt][3]));
+                        a = xor32_max(xor16_max(a));
+                        float tq = a * inv_u_p;
+                        if (scale_quotient_near_tie(tq)) tq = a / u_p;
+                        const uint32_t code = e4m3_encode_nonneg(tq);
+                        const float sv = e4m3_decode(code);
+                        const float dd = sv * pp.g_p;
+                        const float inv = dd == 0.0f ? 0.0f : 1.0f / dd;
+#pragma unroll
+                        for (int i = 0; i < 4; i += 2) {
+                            const f32x2 d = e2m1_pair<0>(e2m1_pack2<0>(0u, pv[tt][i] * inv, pv[tt][i + 1] * inv));
+                            ph[tt][i] = d[0] * sv;
+                            ph[tt][i + 1] = d[1] * sv;
+                        }
+                    }
+                }
             } else {
-                const bf16x8 bp = as_bf16x8(pack8_exact<false>(pp8));
+                // unquantized: fp16 hi + lo (fp16 V), or three bf16 parts (bf16 V)
 #pragma unroll
-                for (int c = 0; c < 32; ++c) o[c] = mfma16x16x32(as_bf16x8(vt_frag(c)), bp, o[c]);
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = pv[tt][i];
+                        if (kVF16) {
+                            ph[tt][i] = (float)(_Float16)x;
+                            pm[tt][i] = (float)(_Float16)(x - ph[tt][i]);
+                        } else {
+                            ph[tt][i] = bf16_lo(pack_bf16_rne(x, 0.0f));
+                            const float r = x - ph[tt][i];
+                            pm[tt][i] = bf16_lo(pack_bf16_rne(r, 0.0f));
+                            plo[tt][i] = bf16_lo(pack_bf16_rne(r - pm[tt][i], 0.0f));
+                        }
+                    }
+                sweeps = kVF16 ? 2 : 3;
+            }
+            // ---- O^T += V^T P^T: V^T fragment of column tile c by transposing
+            // reads (tokens 4gq + s/4 and 16 + 4gq + s/4 in each 16-lane group)
+            const uint16_t* vb1 = sm.vt + (4 * gq + (c16 >> 2)) * kPitch + 4 * (c16 & 3);
+            const uint16_t* vb2 = sm.vt + (16 + 4 * gq + (c16 >> 2)) * kPitch + 4 * (c16 & 3);
+            auto vt_frag = [&](int c) {
+                const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(vb1 + 16 * c)));
+                const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(vb2 + 16 * c)));
+                const u32x2 y1 = __builtin_bit_cast(u32x2, x1), y2 = __builtin_bit_cast(u32x2, x2);
+                return u32x4{y1[0], y1[1], y2[0], y2[1]};
+            };
+            for (int sw = 0; sw < sweeps; ++sw) {
+                float pp8[8];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pp8[4 * tt + i] = sw == 0 ? ph[tt][i] : (sw == 1 ? pm[tt][i] : plo[tt][i]);
+                const u32x4 bp = kVF16 ? u32x4{pack_f16(pp8[0], pp8[1]), pack_f16(pp8[2], pp8[3]),
+                                               pack_f16(pp8[4], pp8[5]), pack_f16(pp8[6], pp8[7])}
+                                       : pack8_exact<false>(pp8);
+                // two column tiles per step, fragments one step ahead of their products
+                u32x4 va = vt_frag(0), vb = vt_frag(1);
+#pragma unroll
+                for (int c = 0; c < 32; c += 2) {
+                    u32x4 na = va, nb = vb;
+                    if (c + 2 < 32) {
+                        na = vt_frag(c + 2);
+                        nb = vt_frag(c + 3);
+                    }
+                    if (kVF16) {
+                        o[c] = mfma_f16(__builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, bp), o[c]);
+                        o[c + 1] = mfma_f16(__builtin_bit_cast(f16x8, vb), __builtin_bit_cast(f16x8, bp), o[c + 1]);
+                    } else {
+                        o[c] = mfma16x16x32(as_bf16x8(va), as_bf16x8(bp), o[c]);
+                        o[c + 1] = mfma16x16x32(as_bf16x8(vb), as_bf16x8(bp), o[c + 1]);
+                    }
+                    if (c + 2 < 32) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    va = na;
+                    vb = nb;
+                }
             }
         }
         if (tid < kTile) walk_store(t + 2);
