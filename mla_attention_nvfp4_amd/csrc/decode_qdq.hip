@@ -263,8 +263,8 @@ void decode_qdq_kernel(QdqParams pp) {
     // Page walk of tile t into offset slot t % 3 by threads 0..31, two tiles
     // ahead: the page-table entry of tile t + 2 is requested at the start of
     // tile t and its offsets stored at the end, so that the load overlaps the
-    // tile's work; a raw cache's K words of tile t + 1 are loaded during tile
-    // t's products (registers kw).
+    // tile's work; a raw cache's K words of tile t + 1 are loaded after tile
+    // t's score products and land during its softmax and PV (registers kw).
     constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + kThreads - 1) / kThreads;   // K: 32 tokens x 36 blocks of 16 features
     u32x4 kw[kKIt][2];
     auto load_k_raw = [&](const int64_t* offs) {
