@@ -30,6 +30,14 @@
  *  - Only gfx950 devices are supported (MLA_ERR_UNSUPPORTED_DEVICE otherwise),
  *    the analogue of [B12X], review 1's point that the NVFP4 kernels need a
  *    guard for the one architecture they were built for.
+ *  - A dispatch counts each grid dimension's work-items in 32 bits, so every
+ *    launch of a call must fit below 2^32 of them.  A request that would not
+ *    is refused with MLA_ERR_UNSUPPORTED, and the caller splits it: more than
+ *    268,435,440 tokens in one NVFP4 cache write or 67,108,860 in one raw
+ *    cache write, T * H or a sequence length above 268,435,440 in one
+ *    prefill (its keys, in the attention call), a context above 67,108,860
+ *    tokens in one gather, or more than 2^32 (row, 16-column block) pairs,
+ *    rows padded to 128 and blocks to 4, in one row quantization.
  */
 #ifndef MLA_NVFP4_H
 #define MLA_NVFP4_H
@@ -299,6 +307,7 @@ int mla_raw_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride,
  *
  *  partial_out  fp32 [B, S, H, D];  partial_lse fp32 [B, S, H]
  *  out          fp32 [B, H, D];     lse fp32 [B, H] or NULL
+ *  B            0..65535;  H  1..65536
  *  D            multiple of 4, 1..4096 */
 int mla_lse_merge(const float* partial_out, const float* partial_lse,
                   const int32_t* splits_per_seq, int B, int S, int H, int D,
@@ -333,7 +342,7 @@ int mla_lse_merge(const float* partial_out, const float* partial_lse,
  *  v            bf16 [T, H, 128], strides (v_stride_t, v_stride_h), same rule;
  *               q, k and v hold finite values (non-finite inputs give
  *               unspecified outputs)
- *  cu_seqlens   int32 [N + 1], non-decreasing, cu[0] = 0, cu[N] = T
+ *  cu_seqlens   int32 [N + 1], non-decreasing, cu[0] = 0, cu[N] = T; N <= 65535
  *  max_seqlen   >= every sequence length
  *  g_*          finite, > 0 (ignored when the flag is off)
  *  workspace    >= mla_prefill_workspace_bytes(T, H, qdq_flags) bytes
@@ -374,7 +383,7 @@ int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
  *  q            bf16 [T_q, H, 192]; k bf16 [T_k, H, 192]; v bf16 [T_k, H, 128]
  *               (strides as in mla_prefill_nvfp4_out; finite values)
  *  cu_seqlens_q int32 [N + 1], cu_seqlens_k int32 [N + 1] (context only),
- *               non-decreasing from 0 to T_q and T_k
+ *               non-decreasing from 0 to T_q and T_k; N <= 65535
  *  max_seqlen_q, max_seqlen_k  >= every sequence's query / key count
  *  workspace    >= mla_prefill_workspace_bytes(T_k, H, qdq_flags) bytes
  *               (T_q when causal)
@@ -411,7 +420,7 @@ int mla_prefill_attention(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
  *
  *  cache        uint8 [num_pages * page_size, record_bytes] (432 or 368)
  *  page_table   int32 [N, max_pages_per_seq]
- *  cu_ctx       int32 [N + 1], non-decreasing from 0 to T_ctx
+ *  cu_ctx       int32 [N + 1], non-decreasing from 0 to T_ctx; N <= 65535
  *  ctx_start    int32 [N] or NULL
  *  max_ctx_len  >= every cu_ctx[n+1] - cu_ctx[n]
  *  kv_c_out     bf16 [T_ctx, 512], row stride (multiple of 8, 16-byte aligned)

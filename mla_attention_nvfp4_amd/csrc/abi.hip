@@ -36,6 +36,18 @@ int ok() {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A dispatch counts the work-items of each grid dimension in 32 bits, so a
+// launch dimension of 256-lane workgroups holds fewer than 2^24 of them.
+// Requests whose launches would need more are refused; the caller splits
+// them.
+constexpr int64_t kMaxBlocks256 = (int64_t(1) << 24) - 1;
+int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }   // a >= 0, b > 0
+bool blocks_fit(int64_t blocks) { return blocks >= 0 && blocks <= kMaxBlocks256; }
+int too_large(const char* what) {
+    return fail(MLA_ERR_UNSUPPORTED, "%s: one launch would exceed 2^32 work-items in a grid dimension; split the call",
+                what);
+}
+
 // Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
@@ -225,7 +237,7 @@ int mla_prefill_p_tile(void) { return mla::prefill_p_tile(); }
 int mla_raw_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride, const uint16_t* k_pe, int64_t k_pe_row_stride,
                         const int64_t* slot_mapping, int64_t T, uint8_t* cache, int64_t num_slots, void* stream) {
     if (T < 0 || num_slots < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "T and num_slots must be >= 0");
-    if (T > (int64_t)INT32_MAX * 4) return fail(MLA_ERR_INVALID_ARGUMENT, "T too large");
+    if (!blocks_fit(cdiv(T, 4))) return too_large("raw cache write");   // 4 tokens per workgroup
     if (T == 0) return ok();
     if (!kv_c || !k_pe || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (kv_c_row_stride % 8 || k_pe_row_stride % 8 || kv_c_row_stride < MLA_D_LATENT || k_pe_row_stride < MLA_D_ROPE ||
@@ -311,7 +323,7 @@ int mla_nvfp4_cache_write(const uint16_t* kv_c, int64_t kv_c_row_stride, const u
     if (T < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "T must be >= 0");
     if (!finite_pos(outer_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "outer_scale must be finite and > 0");
     if (num_slots < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_slots must be >= 0");
-    if (T > (int64_t)INT32_MAX * 4) return fail(MLA_ERR_INVALID_ARGUMENT, "T too large");
+    if (!blocks_fit(cdiv(T, 16))) return too_large("cache write");   // 16 tokens per workgroup
     if (T == 0) return ok();
     if (!kv_c || !k_pe || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (kv_c_row_stride % 8 || !aligned(kv_c, 16) || kv_c_row_stride < MLA_D_LATENT)
@@ -407,8 +419,9 @@ int mla_sparse_decode_nvfp4(const uint16_t* q_nope, const uint16_t* q_rope, int6
 
 int mla_lse_merge(const float* partial_out, const float* partial_lse, const int32_t* splits_per_seq, int B, int S,
                   int H, int D, float* out, float* lse, void* stream) {
-    if (B < 0 || S < 1 || H < 1 || D < 4 || D > 4096 || D % 4)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "need B >= 0, S >= 1, H >= 1, D in [4, 4096] multiple of 4");
+    if (B < 0 || B > 65535 || S < 1 || H < 1 || H > 65536 || D < 4 || D > 4096 || D % 4)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= B <= 65535, S >= 1, 1 <= H <= 65536, D in [4, 4096] "
+                    "multiple of 4");
     if (B == 0) return ok();
     if (!partial_out || !partial_lse || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (!aligned(partial_out, 16) || !aligned(out, 16))
@@ -462,12 +475,15 @@ int mla_prefill_nvfp4_out(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
                           float softmax_scale, unsigned qdq_flags, float g_q, float g_k, float g_v, float g_p,
                           float out_global_scale, void* workspace, size_t workspace_bytes, uint8_t* out_fp4,
                           uint8_t* out_scales, float* lse, void* stream) {
-    if (N < 0 || T < 0 || H < 1 || H > 1024 || max_seqlen < 0)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "need N >= 0, T >= 0, 1 <= H <= 1024, max_seqlen >= 0");
+    if (N < 0 || N > 65535 || T < 0 || H < 1 || H > 1024 || max_seqlen < 0)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= N <= 65535, T >= 0, 1 <= H <= 1024, max_seqlen >= 0");
     int rc0 = check_prefill_flags(qdq_flags, softmax_scale, g_q, g_k, g_v, g_p);
     if (rc0) return rc0;
     if (!finite_pos(out_global_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "out_global_scale must be finite and > 0");
     if (T > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "T must fit in int32");
+    // the K / V pre-passes: 12 and 16 work-items per (row, head), and 16 rows
+    // of a sequence per workgroup column of V's block quantization
+    if (!blocks_fit(cdiv(T * H, 16)) || !blocks_fit(cdiv(max_seqlen, 16))) return too_large("prefill");
     if (T == 0 || N == 0) return ok();
     if (!q || !k || !v || !cu_seqlens || !out_fp4 || !out_scales)
         return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -516,14 +532,16 @@ int mla_prefill_attention(const uint16_t* q, int64_t q_stride_t, int64_t q_strid
                           void* workspace, size_t workspace_bytes, float* out, int64_t out_stride_t,
                           int64_t out_stride_h, float* lse, int64_t lse_stride_t, int64_t lse_stride_h,
                           void* stream) {
-    if (N < 0 || T_q < 0 || H < 1 || H > 1024 || max_seqlen_q < 0)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "need N >= 0, T_q >= 0, 1 <= H <= 1024, max_seqlen_q >= 0");
+    if (N < 0 || N > 65535 || T_q < 0 || H < 1 || H > 1024 || max_seqlen_q < 0)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= N <= 65535, T_q >= 0, 1 <= H <= 1024, max_seqlen_q >= 0");
     if (!causal && (T_k < 0 || max_seqlen_k < 0))
         return fail(MLA_ERR_INVALID_ARGUMENT, "need T_k >= 0 and max_seqlen_k >= 0");
     int rc = check_prefill_flags(qdq_flags, softmax_scale, g_q, g_k, g_v, g_p);
     if (rc) return rc;
     const int64_t Tk = causal ? T_q : T_k;
     if (T_q > INT32_MAX || Tk > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "T_q and T_k must fit in int32");
+    if (!blocks_fit(cdiv(Tk * H, 16)) || !blocks_fit(cdiv(causal ? max_seqlen_q : max_seqlen_k, 16)))
+        return too_large("prefill attention");   // the K / V pre-passes over the keys
     if (T_q == 0 || N == 0) return ok();
     if (!q || !cu_seqlens_q || !out || (!causal && !cu_seqlens_k) || (Tk > 0 && (!k || !v)))
         return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -573,9 +591,10 @@ int mla_nvfp4_cache_gather(const uint8_t* cache, int64_t num_pages, int record_b
                            int64_t k_pe_row_stride, void* stream) {
     int rc = check_record(record_bytes);
     if (rc) return rc;
-    if (N < 0 || T_ctx < 0 || max_ctx_len < 0 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "need N, T_ctx, max_ctx_len >= 0 and page_size, max_pages_per_seq, "
-                    "num_pages >= 1");
+    if (N < 0 || N > 65535 || T_ctx < 0 || max_ctx_len < 0 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "need 0 <= N <= 65535, T_ctx, max_ctx_len >= 0 and page_size, "
+                    "max_pages_per_seq, num_pages >= 1");
+    if (!blocks_fit(cdiv(max_ctx_len, 4))) return too_large("cache gather");
     if ((int64_t)max_pages_per_seq * page_size > INT32_MAX)
         return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq * page_size exceeds int32");
     if (!finite_pos(outer_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "outer_scale must be finite and > 0");
@@ -600,6 +619,10 @@ int mla_nvfp4_quantize_rows(const float* x, int64_t M, int K, float global_scale
     if (M < 0 || K < 16 || K > 65536 || K % 16)
         return fail(MLA_ERR_INVALID_ARGUMENT, "need M >= 0 and K in [16, 65536], a multiple of 16");
     if (!finite_pos(global_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "global_scale must be finite and > 0");
+    {   // one work-item per (row, padded block column), rows padded to 128
+        const int64_t cpad = ((K / 16) + 3) & ~3;
+        if (M > kMaxBlocks256 * 256 || !blocks_fit(cdiv(cdiv(M, 128) * 128 * cpad, 256))) return too_large("quantize_rows");
+    }
     if (M == 0) return ok();
     if (!x || !codes || !scales_swizzled) return fail(MLA_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (!aligned(x, 16) || !aligned(codes, 8)) return fail(MLA_ERR_INVALID_ARGUMENT, "x must be 16-byte and codes 8-byte aligned");

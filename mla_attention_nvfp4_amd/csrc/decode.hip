@@ -651,11 +651,12 @@ __device__ __forceinline__ float wave_sum64(float v) {
 
 template <bool kSparse>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
-    // Workgroup: sequence b, heads 4hq..4hq+3.  When B is a multiple of 8,
-    // sequence b's workgroups are placed on XCD b % 8, where the decode
-    // kernels ran all of its splits, so the partials are read from the L2
-    // they were written to (a bijection; otherwise the identity).
-    const int HQ = (p.H + 3) / 4, wg = (int)blockIdx.x;
+    // Workgroup: sequence b, heads 4hq..4hq+3, on a (HQ, B) grid dispatched
+    // in linear order.  When B is a multiple of 8, sequence b's workgroups
+    // are placed on XCD b % 8, where the decode kernels ran all of its
+    // splits, so the partials are read from the L2 they were written to (a
+    // bijection; otherwise the identity).
+    const int HQ = (p.H + 3) / 4, wg = (int)(blockIdx.x + gridDim.x * blockIdx.y);
     int b, hq;
     if ((p.B & 7) == 0) {
         const int k = wg >> 3;
@@ -759,10 +760,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs p) {
 // rows are then read four splits at a time, added in split order.  More
 // splits take a plain loop over the splits.
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // grid (heads / 4, B): wavefront w of workgroup (x, b) merges head 4x + w
+    const int b = blockIdx.y, h = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (wid >= a.B * a.H) return;
-    const int b = wid / a.H, h = wid % a.H;
+    if (h >= a.H) return;
     int n = a.splits_per_seq ? a.splits_per_seq[b] : a.S;
     n = n < 0 ? 0 : (n > a.S ? a.S : n);
     const int64_t base = (int64_t)b * a.S * a.H + h;  // row of split s: base + s*H
@@ -857,11 +858,12 @@ hipError_t launch_decode_pq(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.B * ((a.H + 3) / 4);   // (sequence, 4 heads)
+    if (a.B == 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.H + 3) / 4), (unsigned)a.B);   // (4 heads, sequence)
     if (a.indices)
-        hipLaunchKernelGGL((split_merge_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_merge_kernel<true>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((split_merge_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_merge_kernel<false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -872,9 +874,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
-    const int waves = a.B * a.H;
-    if (waves == 0) return hipSuccess;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    if (a.B == 0 || a.H == 0) return hipSuccess;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((a.H + 3) / 4), (unsigned)a.B), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

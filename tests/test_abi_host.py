@@ -90,6 +90,25 @@ def test_other_entry_points_reject_invalid_arguments():
     assert lib.mla_prefill_nvfp4_out(*pf, 16, 1., 1., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -1
     assert lib.mla_prefill_nvfp4_out(*pf, 15, 1., 0., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -1
     assert lib.mla_prefill_nvfp4_out(*pf, 15, 1., 1., 1., 1., 0., None, 0, 1 << 20, 1 << 20, None, None) == -1
+    # batch limits: N of the prefill calls and the gather, B and H of the merge
+    pf_n = list(pf)
+    pf_n[10] = 65536
+    assert lib.mla_prefill_nvfp4_out(*pf_n, 15, 1., 1., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -1
+    assert lib.mla_lse_merge(1 << 20, 1 << 20, None, 65536, 2, 1, 4, 1 << 20, 1 << 20, None) == -1
+    assert lib.mla_lse_merge(1 << 20, 1 << 20, None, 1, 2, 65537, 4, 1 << 20, 1 << 20, None) == -1
+    assert lib.mla_nvfp4_cache_gather(1 << 20, 16, 432, 64, 1 << 20, 4, 1 << 20, None, 65536, 64, 64, 1.0,
+                                      1 << 20, 512, 1 << 20, 64, None) == -1
+    # launches beyond 2^32 work-items in a grid dimension: refused as unsupported (-6)
+    big = 16 * ((1 << 24) - 1) + 1
+    assert lib.mla_nvfp4_cache_write(1 << 20, 576, 1 << 20, 576, 1 << 20, big, 1 << 20, 10, 432, 1.0, None) == -6
+    assert lib.mla_raw_cache_write(1 << 20, 576, 1 << 20, 576, 1 << 20, 4 * ((1 << 24) - 1) + 1, 1 << 20, 10,
+                                   None) == -6
+    pf_t = list(pf)
+    pf_t[12] = 1 << 20   # T with H = 4: T * H above 2^28
+    pf_t[11] = 16
+    pf_t[13] = 1024
+    assert lib.mla_prefill_nvfp4_out(*pf_t, 15, 1., 1., 1., 1., 1., None, 0, 1 << 20, 1 << 20, None, None) == -6
+    assert lib.mla_nvfp4_quantize_rows(1 << 20, 1 << 30, 4096, 1.0, 1 << 20, 1 << 20, None) == -6
     # quantize_rows: K must be a multiple of 16
     assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 24, 1.0, 1 << 20, 1 << 20, None) == -1
     assert lib.mla_nvfp4_quantize_rows(1 << 20, 4, 32, 0.0, 1 << 20, 1 << 20, None) == -1
