@@ -276,10 +276,6 @@ void decode_kernel(DecodeArgs p) {
         if (lane < kTile) sm.offs[slot][lane] = off < 0 ? 0 : off;   // masked: record 0, zeroed later
         if (lane == 0) sm.valid[slot] = (uint32_t)vm;
     };
-    auto compute_offs = [&](int t, int slot) {
-        const int pos = position_of(t);
-        store_offs(slot, offset_of(pos, page_of(pos)));
-    };
 
     // ---- staging: this wavefront's records kRpw*w .. +kRpw-1 of a tile in
     // registers.  Lane l holds code word l (elements 8l..8l+7) and the
