@@ -53,7 +53,7 @@ constexpr int kHeadsPerGroup = 16 * kWaves;
 // Q k-steps kept in LDS (B-operand layout, 16 B per lane): the first
 // kQLdsLatent latent k-steps and the two RoPE k-steps; the others stay in
 // registers.
-constexpr int kQLdsLatent = 6;
+constexpr int kQLdsLatent = 8;
 constexpr int kQLds = kQLdsLatent + 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -70,6 +70,16 @@ struct QdqSmem {
     int64_t offs[3][kTile];        // record byte offsets of tiles t .. t+2 (masked tokens: 0)
     uint32_t valid[3];             // bit i: token i of the tile is unmasked
 };
+
+// The lane's index within its wavefront, read afresh (v_mbcnt) where it is
+// used: the volatile statement is not moved out of the tile loop, so values
+// derived from the lane (masks, addresses) are formed in the loop body
+// instead of each holding a register, or a spill slot, across the loop.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -120,6 +130,12 @@ struct QdqParams {
     DecodeArgs d;
     unsigned flags;           // 1 Q, 2 K, 4 P, 8 V; 16/32/64/128 FP8 formats
     float g_q, g_k, g_v, g_p;
+    // Per-call constants formed on the host in IEEE fp32 (the same values the
+    // device would compute), so that they stay in scalar registers rather
+    // than a vector register per lane: 1/g_k, 1/g_v, 1/g_p, the unit 6 g_p of
+    // P's block scales and its reciprocal, the RoPE score multiplier and the
+    // output multiplier.
+    float inv_g_k, inv_g_v, inv_g_p, u_p, inv_u_p, sc_rope, v_mul;
 };
 
 // kCache: 0 NVFP4 records with bf16 RoPE, 1 NVFP4 with e4m3 RoPE, 2 raw bf16
@@ -178,7 +194,7 @@ void decode_qdq_kernel(QdqParams pp) {
     // spans lanes gq and gq ^ 1) or per-tensor FP8, the exact values kept.
     // Raw with fp16 K: scaled by 2^(14 - E) per head (exact).
     // (k-steps kQLdsLatent..15 in registers qf, the others in LDS sm.qs)
-    float q_mul_lat = 1.0f, q_mul_rope = 1.0f;
+    float q_mul_lat = 1.0f;
     u32x4 qf[16 - kQLdsLatent];
     {
         const int64_t qoff = (int64_t)b * p.q_stride_b + (int64_t)(hok ? hq : 0) * p.q_stride_h + 8 * gq;
@@ -221,7 +237,7 @@ void decode_qdq_kernel(QdqParams pp) {
                     }
                 }
             }
-            q_mul_lat = q_mul_rope = pp.g_q;
+            q_mul_lat = pp.g_q;
         } else if (kKF16) {
             float amax = 0.0f;
 #pragma unroll
@@ -248,11 +264,10 @@ void decode_qdq_kernel(QdqParams pp) {
     // multipliers of the stored operands: NVFP4 latent * outer; raw K or V
     // quantized * g_k, g_v; P quantized * g_p
     const float k_mul_lat = kRaw ? (qK ? pp.g_k : 1.0f) : p.outer_scale;
-    const float k_mul_rope = (kRaw && qK) ? pp.g_k : 1.0f;
     const float sc_lat = p.softmax_scale * kLog2e * q_mul_lat * k_mul_lat;
-    const float sc_rope = p.softmax_scale * kLog2e * q_mul_rope * k_mul_rope;
-    const float v_mul = (kRaw ? (qV ? pp.g_v : 1.0f) : p.outer_scale) * (qP ? pp.g_p : 1.0f);
-    const float u_p = 6.0f * pp.g_p, inv_u_p = 1.0f / u_p, inv_g_p = 1.0f / pp.g_p;
+    const float sc_rope = pp.sc_rope, v_mul = pp.v_mul;
+    const float u_p = pp.u_p, inv_u_p = pp.inv_u_p, inv_g_p = pp.inv_g_p;
+    const float inv_gk = pp.inv_g_k, inv_gv = pp.inv_g_v;
 
     f32x4 o[32];
 #pragma unroll
@@ -268,10 +283,13 @@ void decode_qdq_kernel(QdqParams pp) {
     constexpr int kKBlk = kTile * 36, kKIt = (kKBlk + kThreads - 1) / kThreads;   // K: 32 tokens x 36 blocks of 16 features
     u32x4 kw[kKIt][2];
     auto load_k_raw = [&](const int64_t* offs) {
-        // (indices clamped, so every address is a record of the tile)
+        // (indices clamped, so every address is a record of the tile;
+        // wavefronts with no block at step j load nothing)
+        const int t0 = 64 * w + lane_now();
 #pragma unroll
         for (int j = 0; j < kKIt; ++j) {
-            const int i = min(tid + kThreads * j, kKBlk - 1);
+            if (kThreads * j + 64 * w >= kKBlk) break;
+            const int i = min(t0 + kThreads * j, kKBlk - 1);
             const u32x4* src = reinterpret_cast<const u32x4*>(cache + offs[i / 36] + 32 * (i % 36));
             kw[j][0] = src[0];
             kw[j][1] = src[1];
@@ -309,14 +327,16 @@ void decode_qdq_kernel(QdqParams pp) {
     for (int t = 0; t < ntiles; ++t) {
         if (tid < kTile) walk_request(t + 2);
         const int64_t* offs = sm.offs[t % 3];
-        const uint32_t vmask = sm.valid[t % 3];
+        // (one word for the workgroup: read into a scalar register; the
+        // masks below shift it per tile rather than testing loop-invariant
+        // bit masks, which would each hold a register across the loop)
+        const uint32_t vmask = __builtin_amdgcn_readfirstlane(sm.valid[t % 3]);
         // ---- staging
         if constexpr (!kRaw) {
             // 32 tokens x 64 chunks of 8 latent elements: code word + block scale
 #pragma unroll
             for (int k = 0; k < 2048 / kThreads; ++k) {
-                const int c = tid + kThreads * k;
-                const int tok = c >> 6, ch = c & 63;
+                const int tok = w + (kThreads / 64) * k, ch = lane;   // chunk tid + kThreads k
                 const uint8_t* rp = cache + offs[tok];
                 const uint32_t cw = *reinterpret_cast<const uint32_t*>(rp + 4 * ch);
                 const float scf = ((vmask >> tok) & 1u) ? e4m3_decode(rp[256 + (ch >> 1)]) : 0.0f;
@@ -350,11 +370,11 @@ void decode_qdq_kernel(QdqParams pp) {
             // loaded during the previous tile; V: 2 blocks of 16 tokens
             // (absolute positions base, base + 16) x 256 pairs of dims,
             // all loads issued before any is used.
-            const int half = tid >> 8, d0 = 2 * (tid & 255);
-            const float inv_gk = 1.0f / pp.g_k;
+            const int half = __builtin_amdgcn_readfirstlane(tid >> 8), d0 = 2 * (tid & 255);
+            const int t0 = 64 * w + lane_now();
 #pragma unroll
             for (int j = 0; j < kKIt; ++j) {
-                const int i = tid + kThreads * j;
+                const int i = t0 + kThreads * j;
                 if (i >= kKBlk) break;
                 const int tok = i / 36, blk = i % 36;
                 const bool ok = (vmask >> tok) & 1u;
@@ -385,12 +405,11 @@ void decode_qdq_kernel(QdqParams pp) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(cache + offs[16 * half + i] + 2 * d0);
             {
-                const float inv_gv = 1.0f / pp.g_v;
                 float x[2][16];
+                const uint32_t vh = vmask >> (16 * half);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int tok = 16 * half + i;
-                    const bool ok = (vmask >> tok) & 1u;
+                    const bool ok = (vh >> i) & 1u;
                     x[0][i] = ok ? bf16_lo(vr[i]) : 0.0f;
                     x[1][i] = ok ? bf16_hi(vr[i]) : 0.0f;
                 }
@@ -461,12 +480,12 @@ void decode_qdq_kernel(QdqParams pp) {
             // ---- softmax (log2 units): token 16tt + 4gq + i of head c16
             float z[2][4];
             float mx = -INFINITY;
+            const uint32_t vq = vmask >> ((lane_now() >> 2) & 12);   // bits from token 4 gq
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int tok = 16 * tt + 4 * gq + i;
-                    z[tt][i] = ((vmask >> tok) & 1u) ? sc_lat * sl[tt][i] + sc_rope * sr[tt][i] : -INFINITY;
+                    z[tt][i] = ((vq >> (16 * tt + i)) & 1u) ? sc_lat * sl[tt][i] + sc_rope * sr[tt][i] : -INFINITY;
                     mx = fmaxf(mx, z[tt][i]);
                 }
             mx = xor32_max(xor16_max(mx));
@@ -636,6 +655,21 @@ hipError_t launch_decode_qdq(const DecodeArgs& a, unsigned flags, float g_q, flo
         return launch_decode_pq(b, stream);
     }
     QdqParams pp{a, flags, g_q, g_k, g_v, g_p};
+    {
+        // (the kernel's multipliers: scores ((scale log2 e) q_mul) k_mul with
+        // q_mul = g_q when Q is quantized, k_mul = g_k for a quantized raw K;
+        // output V multiplier times g_p when P is quantized)
+        const bool raw = a.record_bytes == 1152;
+        const float q_mul_rope = (flags & 1u) ? g_q : 1.0f;
+        const float k_mul_rope = (raw && (flags & 2u)) ? g_k : 1.0f;
+        pp.inv_g_k = 1.0f / g_k;
+        pp.inv_g_v = 1.0f / g_v;
+        pp.inv_g_p = 1.0f / g_p;
+        pp.u_p = 6.0f * g_p;
+        pp.inv_u_p = 1.0f / pp.u_p;
+        pp.sc_rope = a.softmax_scale * kLog2e * q_mul_rope * k_mul_rope;
+        pp.v_mul = (raw ? ((flags & 8u) ? g_v : 1.0f) : a.outer_scale) * ((flags & 4u) ? g_p : 1.0f);
+    }
     hipError_t e;
     if (a.record_bytes == 1152) {
         const bool kf = flags & 2u, vf = flags & 8u;
