@@ -101,9 +101,10 @@ __device__ __forceinline__ u32x4 pack8_exact(const float* x) {
 }
 
 // Quantize-dequantize of 16 values along their block: NVFP4 (multiplier g,
-// the exact values s*v are returned, g not applied) or per-tensor FP8
-// (inv_g = fp32(1/g); the exact e4m3 values are returned).
-__device__ __forceinline__ void qdq16(float* x, bool fp8, float g, float inv_g) {
+// u = fp32(6 g) and inv_u = fp32(1/u) given; the exact values s*v are
+// returned, g not applied) or per-tensor FP8 (inv_g = fp32(1/g); the exact
+// e4m3 values are returned).
+__device__ __forceinline__ void qdq16(float* x, bool fp8, float g, float inv_g, float u, float inv_u) {
     if (fp8) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -116,7 +117,7 @@ __device__ __forceinline__ void qdq16(float* x, bool fp8, float g, float inv_g) 
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(x[i]));
-    const Nvfp4Scale sc = nvfp4_block_scale(a, g);
+    const Nvfp4Scale sc = nvfp4_block_scale_fast(a, g, u, inv_u);
     const float sv = e4m3_decode(sc.code);
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -132,10 +133,10 @@ struct QdqParams {
     float g_q, g_k, g_v, g_p;
     // Per-call constants formed on the host in IEEE fp32 (the same values the
     // device would compute), so that they stay in scalar registers rather
-    // than a vector register per lane: 1/g_k, 1/g_v, 1/g_p, the unit 6 g_p of
-    // P's block scales and its reciprocal, the RoPE score multiplier and the
-    // output multiplier.
-    float inv_g_k, inv_g_v, inv_g_p, u_p, inv_u_p, sc_rope, v_mul;
+    // than a vector register per lane: 1/g_k, 1/g_v, 1/g_p, the units 6 g of
+    // K's, V's and P's block scales and their reciprocals, the RoPE score
+    // multiplier and the output multiplier.
+    float inv_g_k, inv_g_v, inv_g_p, u_k, inv_u_k, u_v, inv_u_v, u_p, inv_u_p, sc_rope, v_mul;
 };
 
 // kCache: 0 NVFP4 records with bf16 RoPE, 1 NVFP4 with e4m3 RoPE, 2 raw bf16
@@ -367,9 +368,10 @@ void decode_qdq_kernel(QdqParams pp) {
             }
         } else {
             // K: 32 tokens x 36 blocks of 16 features (32 latent, 4 RoPE),
-            // loaded during the previous tile; V: 2 blocks of 16 tokens
-            // (absolute positions base, base + 16) x 256 pairs of dims,
-            // all loads issued before any is used.
+            // loaded during the previous tile.  The latent words also go to
+            // the V tile as they are (masked tokens 0); a quantized V is then
+            // formed there in place: 2 blocks of 16 tokens (absolute
+            // positions base, base + 16) x 256 pairs of dims.
             const int half = __builtin_amdgcn_readfirstlane(tid >> 8), d0 = 2 * (tid & 255);
             const int t0 = 64 * w + lane_now();
 #pragma unroll
@@ -379,6 +381,12 @@ void decode_qdq_kernel(QdqParams pp) {
                 const int tok = i / 36, blk = i % 36;
                 const bool ok = (vmask >> tok) & 1u;
                 const u32x4 w0 = kw[j][0], w1 = kw[j][1];
+                if (blk < 32) {
+                    const u32x4 zero = {0u, 0u, 0u, 0u};
+                    u32x4* vdst = reinterpret_cast<u32x4*>(&sm.vt[tok * kPitch + 16 * blk]);
+                    vdst[0] = ok ? w0 : zero;
+                    vdst[1] = ok ? w1 : zero;
+                }
                 float x[16];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
@@ -387,7 +395,7 @@ void decode_qdq_kernel(QdqParams pp) {
                     x[8 + 2 * jj] = ok ? bf16_lo(w1[jj]) : 0.0f;
                     x[8 + 2 * jj + 1] = ok ? bf16_hi(w1[jj]) : 0.0f;
                 }
-                if (qK) qdq16(x, fK, pp.g_k, inv_gk);
+                if (qK) qdq16(x, fK, pp.g_k, inv_gk, pp.u_k, pp.inv_u_k);
                 u32x4 a, c;
                 if (blk < 32 && kKF16) {
                     a = pack8_exact<true>(x);
@@ -400,23 +408,19 @@ void decode_qdq_kernel(QdqParams pp) {
                 dst[0] = a;
                 dst[1] = c;
             }
-            // V: per dim the block's amax (NVFP4) or each element (FP8)
-            uint32_t vr[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(cache + offs[16 * half + i] + 2 * d0);
-            {
+            // V quantized: per dim the block's amax (NVFP4) or each element
+            // (FP8); unquantized, the tile already holds the operand
+            if (qV) {
+                __syncthreads();   // the V tile's raw words are all written
                 float x[2][16];
-                const uint32_t vh = vmask >> (16 * half);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const bool ok = (vh >> i) & 1u;
-                    x[0][i] = ok ? bf16_lo(vr[i]) : 0.0f;
-                    x[1][i] = ok ? bf16_hi(vr[i]) : 0.0f;
+                    const uint32_t r = *reinterpret_cast<const uint32_t*>(&sm.vt[(16 * half + i) * kPitch + d0]);
+                    x[0][i] = bf16_lo(r);
+                    x[1][i] = bf16_hi(r);
                 }
-                if (qV) {
 #pragma unroll
-                    for (int d = 0; d < 2; ++d) qdq16(x[d], fV, pp.g_v, inv_gv);
-                }
+                for (int d = 0; d < 2; ++d) qdq16(x[d], fV, pp.g_v, inv_gv, pp.u_v, pp.inv_u_v);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tok = 16 * half + i;
@@ -665,6 +669,10 @@ hipError_t launch_decode_qdq(const DecodeArgs& a, unsigned flags, float g_q, flo
         pp.inv_g_k = 1.0f / g_k;
         pp.inv_g_v = 1.0f / g_v;
         pp.inv_g_p = 1.0f / g_p;
+        pp.u_k = 6.0f * g_k;
+        pp.inv_u_k = 1.0f / pp.u_k;
+        pp.u_v = 6.0f * g_v;
+        pp.inv_u_v = 1.0f / pp.u_v;
         pp.u_p = 6.0f * g_p;
         pp.inv_u_p = 1.0f / pp.u_p;
         pp.sc_rope = a.softmax_scale * kLog2e * q_mul_rope * k_mul_rope;
