@@ -307,7 +307,7 @@ void decode_kernel(DecodeArgs p) {
     // lane = 16-byte column chunk (8 latent elements)
     auto dequant = [&](int kbuf, int slot) {
         uint16_t* ks = sm.ks[kbuf];
-        const uint32_t vmask = sm.valid[slot];
+        const uint32_t vmask = __builtin_amdgcn_readfirstlane(sm.valid[slot]);   // (one word)
         bool big = false;
 #pragma unroll
         for (int r = 0; r < kRpw; ++r) {
@@ -410,11 +410,12 @@ void decode_kernel(DecodeArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) z[tt][i] = score_scale * sa[tt][i];
         if (vmask != 0xffffffffu) {   // (uniform) a tile with masked tokens
+            const uint32_t vq = vmask >> ((lane_now() >> 2) & 12);   // bits from token 4 gq
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (!((vmask >> (16 * tt + 4 * gq + i)) & 1u)) z[tt][i] = -INFINITY;
+                    if (!((vq >> (16 * tt + i)) & 1u)) z[tt][i] = -INFINITY;
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)

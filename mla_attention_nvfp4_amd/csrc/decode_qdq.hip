@@ -71,16 +71,6 @@ struct QdqSmem {
     uint32_t valid[3];             // bit i: token i of the tile is unmasked
 };
 
-// The lane's index within its wavefront, read afresh (v_mbcnt) where it is
-// used: the volatile statement is not moved out of the tile loop, so values
-// derived from the lane (masks, addresses) are formed in the loop body
-// instead of each holding a register, or a spill slot, across the loop.
-__device__ __forceinline__ int lane_now() {
-    int l;
-    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-    return l;
-}
-
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

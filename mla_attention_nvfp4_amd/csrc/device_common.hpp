@@ -114,6 +114,16 @@ __device__ __forceinline__ f32x2 e2m1_pair(uint32_t w) {
 // multiplier g: t = a / (6 g), s = e4m3(t), d = s * g, inv = 1/d (0 when
 // d == 0); each step one IEEE fp32 operation (this file is compiled with
 // contraction off and correctly rounded division).
+// The lane's index within its wavefront, read afresh (v_mbcnt) where it is
+// used: the volatile statement is not moved out of a loop, so values
+// derived from the lane (masks, addresses) are formed in the loop body
+// instead of each holding a register, or a spill slot, across the loop.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 struct Nvfp4Scale {
     uint32_t code;
     float inv;
