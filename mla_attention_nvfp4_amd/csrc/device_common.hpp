@@ -108,12 +108,6 @@ __device__ __forceinline__ f32x2 e2m1_pair(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kSel);
 }
 
-// ------------------------------------------------------- NVFP4 blocks --
-
-// Two-level NVFP4 block scale for a block with amax `a` and dequant
-// multiplier g: t = a / (6 g), s = e4m3(t), d = s * g, inv = 1/d (0 when
-// d == 0); each step one IEEE fp32 operation (this file is compiled with
-// contraction off and correctly rounded division).
 // The lane's index within its wavefront, read afresh (v_mbcnt) where it is
 // used: the volatile statement is not moved out of a loop, so values
 // derived from the lane (masks, addresses) are formed in the loop body
@@ -124,6 +118,12 @@ __device__ __forceinline__ int lane_now() {
     return l;
 }
 
+// ------------------------------------------------------- NVFP4 blocks --
+
+// Two-level NVFP4 block scale for a block with amax `a` and dequant
+// multiplier g: t = a / (6 g), s = e4m3(t), d = s * g, inv = 1/d (0 when
+// d == 0); each step one IEEE fp32 operation (this file is compiled with
+// contraction off and correctly rounded division).
 struct Nvfp4Scale {
     uint32_t code;
     float inv;
