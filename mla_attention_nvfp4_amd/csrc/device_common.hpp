@@ -154,7 +154,15 @@ __device__ __forceinline__ bool scale_quotient_near_tie(float tq) {
 // inv are those of nvfp4_block_scale.
 __device__ __forceinline__ Nvfp4Scale nvfp4_block_scale_fast(float a, float g, float u, float inv_u) {
     float t = a * inv_u;
-    if (scale_quotient_near_tie(t)) t = a / u;
+    const bool near = scale_quotient_near_tie(t);
+    if (__any(near)) {
+        // (a wavefront divides only when one of its lanes needs it; the empty
+        // statement keeps the compiler from computing the quotient in every
+        // lane and selecting it)
+        __asm__ volatile("");
+        const float q = a / u;
+        t = near ? q : t;
+    }
     const uint32_t s = e4m3_encode_nonneg(t);
     const float d = e4m3_decode(s) * g;
     return Nvfp4Scale{s, (d == 0.0f) ? 0.0f : 1.0f / d};
