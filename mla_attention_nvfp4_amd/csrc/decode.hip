@@ -473,7 +473,12 @@ void decode_kernel(DecodeArgs p) {
                     float a = fmaxf(fmaxf(pv[tt][0], pv[tt][1]), fmaxf(pv[tt][2], pv[tt][3]));
                     a = xor32_max(xor16_max(a));
                     float tq = a * p_inv_u;
-                    if (scale_quotient_near_tie(tq)) tq = a / p_u;
+                    const bool near = scale_quotient_near_tie(tq);
+                    if (__any(near)) {   // (the exact division only when a lane needs it)
+                        __asm__ volatile("");
+                        const float q = a / p_u;
+                        tq = near ? q : tq;
+                    }
                     const uint32_t code = e4m3_encode_nonneg(tq);
                     const float sv = e4m3_decode(code);
                     const float dd = sv * p.g_p;
